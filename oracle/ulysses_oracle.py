@@ -1,0 +1,374 @@
+"""Plain fp64 CPU oracle of the Ulysses per-rank hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or run
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+library and imports nothing from it.
+
+What it computes (citations name a page and the passage on it):
+
+* seq_to_head / head_to_seq -- the two all-to-all layout changes over P ranks.
+  "Ulysses Sequence Parallelism: A Temporary Change of Layout" (pinyu.ai),
+  section "Use the other independent axis": every sender splits its local heads
+  into P groups, every receiver gathers one group from each sender and
+  concatenates the token blocks along the sequence; the shape goes
+  [B, L/P, H, d_h] -> [B, L, H/P, d_h] and back (section "One attention block,
+  end to end", steps 2 and 4). Rank i owns tokens [i N/P, (i+1) N/P) before
+  and heads [i h/P, (i+1) h/P) after (paper-graph summary of arXiv 2309.14509,
+  section 3.4.1). Implemented as index arithmetic on d_h-element rows; values
+  are moved as raw bits (any dtype).
+
+* attn_fwd -- per-head exact attention O = softmax(Q K^T / sqrt(d_h)) V over the
+  full sequence, with an optional causal mask (paper-graph summary, sections
+  3.4.1 and 3.4.5; pinyu.ai, section "The layout that saves memory breaks at
+  attention"; papers.chlience.com reading note, section 5.1). Two-pass
+  softmax per block of rows in fp64: row max, then sum of exponentials.
+  The log-sum-exp of each row's scaled scores is returned alongside O.
+
+* attn_bwd -- the exact gradient of attn_fwd (the pages train with the method
+  but do not write the backward out; the reading taken is the gradient of the
+  exact attention above). With P = softmax(S), S = Q K^T / sqrt(d_h):
+      dV = P^T dO,  dP = dO V^T,  D_i = sum_e dO_ie O_ie,
+      dS = P o (dP - D),  dQ = dS K / sqrt(d_h),  dK = dS^T Q / sqrt(d_h).
+
+Readings of points the pages leave open (kept in one place):
+  * causal means key j is visible to query i iff j <= i (the diagonal is kept);
+    positions are global token indices after the layout change;
+  * masked keys are excluded from the softmax sum (equivalent to -inf logits);
+  * the scale is exactly 1/sqrt(d_h); no dropout, bias or soft-cap;
+  * the virtual ranks of one GPU sit rank-major in one buffer:
+    seq layout [P, B, L/P, H, d_h], head layout [P, B, L, H/P, d_h].
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+# Rows of the score matrix handled per block: bounds host memory to about
+# ROW_BLOCK * L * 8 bytes per temporary.
+ROW_BLOCK = 256
+
+
+# ---------------------------------------------------------------------------
+# decoding of the raw input bits (exact widening)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(u16: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    u32 = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact value of the kernel's input bits as float64 (bf16 bits or fp32)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# the two layout changes (pinyu.ai "Use the other independent axis";
+# paper-graph summary section 3.4.1)
+# ---------------------------------------------------------------------------
+
+def check_divisible(L: int, H: int, P: int) -> None:
+    """The head count and the length must split evenly over P ranks
+    (pinyu.ai, "Head-count constraints": H % P == 0)."""
+    if P <= 0 or H % P != 0 or L % P != 0:
+        raise ValueError(f"H={H} and L={L} must both be divisible by P={P}")
+
+
+def seq_to_head_source_rows(B: int, L: int, H: int, P: int) -> np.ndarray:
+    """For every destination row of the head layout, the source row of the seq layout.
+
+    Rows are d_h-element vectors. Destination row (p, b, n, j) of
+    [P, B, L, H/P] takes the row of sender rank r = n div (L/P), local token
+    t = n mod (L/P), global head p*(H/P) + j, i.e. row (r, b, t, p*(H/P) + j)
+    of [P, B, L/P, H].
+    """
+    check_divisible(L, H, P)
+    Lp, Hp = L // P, H // P
+    p = np.arange(P, dtype=np.int64)[:, None, None, None]
+    b = np.arange(B, dtype=np.int64)[None, :, None, None]
+    n = np.arange(L, dtype=np.int64)[None, None, :, None]
+    j = np.arange(Hp, dtype=np.int64)[None, None, None, :]
+    r, t = n // Lp, n % Lp
+    src = ((r * B + b) * Lp + t) * H + (p * Hp + j)
+    return src.reshape(-1)
+
+
+def head_to_seq_source_rows(B: int, L: int, H: int, P: int) -> np.ndarray:
+    """For every destination row of the seq layout, the source row of the head layout.
+
+    Destination row (r, b, t, h) of [P, B, L/P, H] takes the row of head-group
+    rank p = h div (H/P), local head j = h mod (H/P), global token
+    n = r*(L/P) + t, i.e. row (p, b, n, j) of [P, B, L, H/P].
+    """
+    check_divisible(L, H, P)
+    Lp, Hp = L // P, H // P
+    r = np.arange(P, dtype=np.int64)[:, None, None, None]
+    b = np.arange(B, dtype=np.int64)[None, :, None, None]
+    t = np.arange(Lp, dtype=np.int64)[None, None, :, None]
+    h = np.arange(H, dtype=np.int64)[None, None, None, :]
+    p, j = h // Hp, h % Hp
+    n = r * Lp + t
+    src = ((p * B + b) * L + n) * Hp + j
+    return src.reshape(-1)
+
+
+def _move_rows(x: np.ndarray, rows: np.ndarray, d: int, out_shape) -> np.ndarray:
+    flat = np.ascontiguousarray(x).reshape(-1, d)
+    return np.take(flat, rows, axis=0).reshape(out_shape)
+
+
+def seq_to_head(x: np.ndarray, B: int, L: int, H: int, d: int, P: int) -> np.ndarray:
+    """[P, B, L/P, H, d] -> [P, B, L, H/P, d] (first all-to-all). Bits are moved, not values."""
+    rows = seq_to_head_source_rows(B, L, H, P)
+    return _move_rows(x, rows, d, (P, B, L, H // P, d))
+
+
+def head_to_seq(y: np.ndarray, B: int, L: int, H: int, d: int, P: int) -> np.ndarray:
+    """[P, B, L, H/P, d] -> [P, B, L/P, H, d] (second all-to-all). Bits are moved, not values."""
+    rows = head_to_seq_source_rows(B, L, H, P)
+    return _move_rows(y, rows, d, (P, B, L // P, H, d))
+
+
+def seq_to_head_part(x: np.ndarray, B: int, L: int, H: int, d: int, P: int, p: int) -> np.ndarray:
+    """Destination rank p's block [B, L, H/P, d] of seq_to_head, for bounded host memory."""
+    rows = seq_to_head_source_rows(B, L, H, P).reshape(P, -1)[p]
+    return _move_rows(x, rows, d, (B, L, H // P, d))
+
+
+# ---------------------------------------------------------------------------
+# exact attention, forward (definition written out, fp64, two-pass softmax)
+# ---------------------------------------------------------------------------
+
+def _visible_keys(i1: int, L: int, causal: bool) -> int:
+    return i1 if causal else L
+
+
+def _scores(qb: np.ndarray, kk: np.ndarray, i0: int, causal: bool, scale: float) -> np.ndarray:
+    """Scaled scores of a row block, masked keys set to -inf (excluded from the sum)."""
+    s = (qb @ kk.T) * scale
+    if causal:
+        rows = np.arange(i0, i0 + qb.shape[0])[:, None]
+        cols = np.arange(kk.shape[0])[None, :]
+        s = np.where(cols <= rows, s, -np.inf)
+    return s
+
+
+def _softmax_rows(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Two-pass softmax: returns probabilities and the log-sum-exp of each row."""
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = np.sum(e, axis=1, keepdims=True)
+    return e / l, (m + np.log(l))[:, 0]
+
+
+def attn_fwd_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
+                  row_block: int = ROW_BLOCK) -> Tuple[np.ndarray, np.ndarray]:
+    """One head: q, k, v [L, d] float64 -> O [L, d], LSE [L]."""
+    L, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    o = np.empty((L, d), dtype=np.float64)
+    lse = np.empty((L,), dtype=np.float64)
+    for i0 in range(0, L, row_block):
+        i1 = min(L, i0 + row_block)
+        nk = _visible_keys(i1, L, causal)
+        s = _scores(q[i0:i1], k[:nk], i0, causal, scale)
+        p, lse[i0:i1] = _softmax_rows(s)
+        o[i0:i1] = p @ v[:nk]
+    return o, lse
+
+
+def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True,
+             row_block: int = ROW_BLOCK) -> Tuple[np.ndarray, np.ndarray]:
+    """Heads are independent: q, k, v [B, L, Hh, d] float64 -> O [B, L, Hh, d], LSE [B, Hh, L]."""
+    B, L, Hh, d = q.shape
+    o = np.empty_like(q, dtype=np.float64)
+    lse = np.empty((B, Hh, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hh):
+            o[b, :, h], lse[b, h] = attn_fwd_head(q[b, :, h], k[b, :, h], v[b, :, h], causal, row_block)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# exact attention, backward (explicit formula, fp64)
+# ---------------------------------------------------------------------------
+
+def attn_bwd_head(q, k, v, do, causal: bool, row_block: int = ROW_BLOCK):
+    """One head: the exact gradient of <dO, O> w.r.t. q, k, v; all [L, d] float64.
+
+    Per row block the probabilities are formed once and used for O, D, dP,
+    dS and the three products; dK and dV accumulate over the row blocks.
+    Returns (dq, dk, dv, o, lse, D).
+    """
+    L, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((L, d))
+    dk = np.zeros((L, d))
+    dv = np.zeros((L, d))
+    o = np.empty((L, d))
+    lse = np.empty((L,))
+    D = np.empty((L,))
+    for i0 in range(0, L, row_block):
+        i1 = min(L, i0 + row_block)
+        nk = _visible_keys(i1, L, causal)
+        s = _scores(q[i0:i1], k[:nk], i0, causal, scale)
+        p, lse[i0:i1] = _softmax_rows(s)
+        ob = p @ v[:nk]
+        o[i0:i1] = ob
+        dob = do[i0:i1]
+        Db = np.sum(dob * ob, axis=1)
+        D[i0:i1] = Db
+        dp = dob @ v[:nk].T
+        ds = p * (dp - Db[:, None])
+        dq[i0:i1] = (ds @ k[:nk]) * scale
+        dk[:nk] += (ds.T @ q[i0:i1]) * scale
+        dv[:nk] += p.T @ dob
+    return dq, dk, dv, o, lse, D
+
+
+def attn_bwd(q, k, v, do, causal: bool = True, row_block: int = ROW_BLOCK):
+    """[B, L, Hh, d] float64 each -> (dq, dk, dv) [B, L, Hh, d], plus o, lse [B,Hh,L], D [B,Hh,L]."""
+    B, L, Hh, d = q.shape
+    dq = np.empty((B, L, Hh, d))
+    dk = np.empty((B, L, Hh, d))
+    dv = np.empty((B, L, Hh, d))
+    o = np.empty((B, L, Hh, d))
+    lse = np.empty((B, Hh, L))
+    D = np.empty((B, Hh, L))
+    for b in range(B):
+        for h in range(Hh):
+            r = attn_bwd_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], causal, row_block)
+            dq[b, :, h], dk[b, :, h], dv[b, :, h], o[b, :, h], lse[b, h], D[b, h] = r
+    return dq, dk, dv, o, lse, D
+
+
+# ---------------------------------------------------------------------------
+# sampled evaluation for sizes where the full quadratic oracle is too slow
+# ---------------------------------------------------------------------------
+
+def attn_rows(q, k, v, rows: Sequence[int], causal: bool = True, do=None):
+    """Forward (and, with dO, the dQ row) of selected query rows of one head.
+
+    q, k, v, do: [L, d] float64 (any array supporting row slicing, e.g. a
+    memory map). Each row costs O(i d). Returns dict with o [n, d], lse [n],
+    and with dO also D [n] and dq [n, d].
+    """
+    L, d = k.shape
+    scale = 1.0 / math.sqrt(d)
+    rows = list(rows)
+    out = {"o": np.empty((len(rows), d)), "lse": np.empty(len(rows))}
+    if do is not None:
+        out["D"] = np.empty(len(rows))
+        out["dq"] = np.empty((len(rows), d))
+    for n, i in enumerate(rows):
+        nk = i + 1 if causal else L
+        kk = np.asarray(k[:nk], dtype=np.float64)
+        vv = np.asarray(v[:nk], dtype=np.float64)
+        qi = np.asarray(q[i], dtype=np.float64)
+        s = (kk @ qi) * scale
+        m = np.max(s)
+        e = np.exp(s - m)
+        l = np.sum(e)
+        p = e / l
+        oi = p @ vv
+        out["o"][n] = oi
+        out["lse"][n] = m + math.log(l)
+        if do is not None:
+            doi = np.asarray(do[i], dtype=np.float64)
+            Di = float(doi @ oi)
+            dp = vv @ doi
+            ds = p * (dp - Di)
+            out["D"][n] = Di
+            out["dq"][n] = (ds @ kk) * scale
+    return out
+
+
+def attn_dkv_cols(q, k, v, do, cols: Sequence[int], causal: bool = True,
+                  row_block: int = ROW_BLOCK):
+    """dK and dV of selected key columns j of one head.
+
+    dK_j = (1/sqrt d) sum_{i sees j} dS_ij q_i and dV_j = sum_{i sees j} P_ij dO_i.
+    Every row i that sees some selected column needs its own LSE_i and D_i,
+    which are formed here from the full row (no value comes from elsewhere).
+    Cost O(#rows-that-see-the-columns * L * d); cheap for columns near the end
+    of a causal sequence.
+    """
+    L, d = k.shape
+    scale = 1.0 / math.sqrt(d)
+    cols = np.asarray(sorted(set(int(c) for c in cols)), dtype=np.int64)
+    first_row = int(cols.min()) if causal else 0
+    dk = np.zeros((len(cols), d))
+    dv = np.zeros((len(cols), d))
+    kc = np.asarray(k[cols], dtype=np.float64)
+    vc = np.asarray(v[cols], dtype=np.float64)
+    for i0 in range(first_row, L, row_block):
+        i1 = min(L, i0 + row_block)
+        nk = _visible_keys(i1, L, causal)
+        qb = np.asarray(q[i0:i1], dtype=np.float64)
+        dob = np.asarray(do[i0:i1], dtype=np.float64)
+        kk = np.asarray(k[:nk], dtype=np.float64)
+        vv = np.asarray(v[:nk], dtype=np.float64)
+        s = _scores(qb, kk, i0, causal, scale)
+        p, _ = _softmax_rows(s)
+        ob = p @ vv
+        Db = np.sum(dob * ob, axis=1)
+        pc = p[:, cols[cols < nk]] if causal else p[:, cols]
+        sel = cols < nk if causal else np.ones(len(cols), bool)
+        dpc = dob @ vc[sel].T
+        dsc = pc * (dpc - Db[:, None])
+        dk[sel] += (dsc.T @ qb) * scale
+        dv[sel] += pc.T @ dob
+    return cols, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# the whole per-layer attention block over P virtual ranks (forward)
+# ---------------------------------------------------------------------------
+
+def ulysses_attention_fwd(q_seq, k_seq, v_seq, B, L, H, d, P, causal=True):
+    """seq_to_head on Q, K, V; attention on every rank's head group; head_to_seq on O.
+
+    Inputs float64 [P, B, L/P, H, d]; returns O in the same layout and the LSE
+    of every rank [P, B, H/P, L]. (pinyu.ai, "One attention block, end to end".)
+    """
+    qh = seq_to_head(q_seq, B, L, H, d, P)
+    kh = seq_to_head(k_seq, B, L, H, d, P)
+    vh = seq_to_head(v_seq, B, L, H, d, P)
+    oh = np.empty_like(qh)
+    lse = np.empty((P, B, H // P, L))
+    for p in range(P):
+        oh[p], lse[p] = attn_fwd(qh[p], kh[p], vh[p], causal)
+    return head_to_seq(oh, B, L, H, d, P), lse
+
+
+def monolithic_attention_fwd(q_seq, k_seq, v_seq, B, L, H, d, P, causal=True):
+    """All H heads on the whole sequence on one device, no layout change.
+
+    The seq buffer [P, B, L/P, H, d] is viewed as the global [B, L, H, d]
+    (rank r's tokens are positions r*L/P ...), attention is run per head, and
+    the result is cut back into the seq buffer.
+    """
+    def glob(x):
+        return np.ascontiguousarray(x.transpose(1, 0, 2, 3, 4)).reshape(B, L, H, d)
+    o, _ = attn_fwd(glob(q_seq), glob(k_seq), glob(v_seq), causal)
+    return np.ascontiguousarray(o.reshape(B, P, L // P, H, d).transpose(1, 0, 2, 3, 4))
+
+
+# ---------------------------------------------------------------------------
+# comparison helpers used by the parity tests
+# ---------------------------------------------------------------------------
+
+def error_stats(x: np.ndarray, ref: np.ndarray) -> Dict[str, float]:
+    """max |x - ref| and ||x - ref||_F / ||ref||_F in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = x - ref
+    nref = float(np.linalg.norm(ref.ravel()))
+    return {"max_abs": float(np.max(np.abs(diff))) if diff.size else 0.0,
+            "rel_fro": float(np.linalg.norm(diff.ravel()) / nref) if nref > 0 else float(np.linalg.norm(diff.ravel()))}

@@ -1,0 +1,398 @@
+"""Pins of the fp64 oracle to facts outside itself (no GPU needed).
+
+Each test ties the oracle to something other than its own formulas: the
+pages' procedural description of the all-to-all, a hand-drawn ownership grid
+(tests/golden), closed forms, invariants of softmax attention, finite
+differences, and library routines (torch's CPU attention and autograd in
+float64). A plausible slip -- a swapped index, a dropped term, a wrong sign,
+scale or mask edge -- breaks at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, custom, f32_to_bf16_bits, host_tensor
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# the all-to-all layout changes
+# ---------------------------------------------------------------------------
+
+def _s2h_by_procedure(x, B, L, H, d, P):
+    """Sender/receiver procedure of pinyu.ai "Use the other independent axis".
+
+    Each sender splits its local heads into P groups; receiver p collects
+    group p from every sender and concatenates the token blocks along the
+    sequence in sender order. Written with explicit lists, no index formula.
+    """
+    Hp = H // P
+    groups = [[x[r][:, :, g * Hp:(g + 1) * Hp, :] for g in range(P)] for r in range(P)]
+    return np.stack([np.concatenate([groups[r][p] for r in range(P)], axis=1) for p in range(P)])
+
+
+def _h2s_by_procedure(y, B, L, H, d, P):
+    """Inverse procedure: each head-group owner cuts its full sequence into P
+    token blocks; token-rank r concatenates block r of every owner along heads."""
+    Lp = L // P
+    blocks = [[y[p][:, r * Lp:(r + 1) * Lp] for r in range(P)] for p in range(P)]
+    return np.stack([np.concatenate([blocks[p][r] for p in range(P)], axis=2) for r in range(P)])
+
+
+SHAPES = [(1, 8, 4, 2, 2), (2, 12, 6, 3, 3), (3, 16, 8, 4, 4), (1, 6, 3, 5, 1), (2, 10, 10, 1, 5),
+          (1, 32, 16, 2, 8)]
+
+
+@pytest.mark.parametrize("B,L,H,d,P", SHAPES)
+def test_s2h_h2s_match_sender_receiver_procedure(B, L, H, d, P):
+    rng = np.random.default_rng(1)
+    x = rng.integers(0, 2**16, size=(P, B, L // P, H, d), dtype=np.uint16)
+    y = oracle.seq_to_head(x, B, L, H, d, P)
+    assert y.shape == (P, B, L, H // P, d)
+    np.testing.assert_array_equal(y, _s2h_by_procedure(x, B, L, H, d, P))
+    z = rng.integers(0, 2**16, size=(P, B, L, H // P, d), dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.head_to_seq(z, B, L, H, d, P), _h2s_by_procedure(z, B, L, H, d, P))
+
+
+@pytest.mark.parametrize("B,L,H,d,P", SHAPES)
+def test_round_trips_and_bijection(B, L, H, d, P):
+    rng = np.random.default_rng(2)
+    x = rng.integers(0, 2**32, size=(P, B, L // P, H, d), dtype=np.uint32)
+    y = oracle.seq_to_head(x, B, L, H, d, P)
+    np.testing.assert_array_equal(oracle.head_to_seq(y, B, L, H, d, P), x)
+    z = rng.integers(0, 2**32, size=(P, B, L, H // P, d), dtype=np.uint32)
+    np.testing.assert_array_equal(oracle.seq_to_head(oracle.head_to_seq(z, B, L, H, d, P), B, L, H, d, P), z)
+    rows = oracle.seq_to_head_source_rows(B, L, H, P)
+    assert np.array_equal(np.sort(rows), np.arange(B * L * H))  # every source row used exactly once
+    rows2 = oracle.head_to_seq_source_rows(B, L, H, P)
+    assert np.array_equal(rows2[rows], np.arange(B * L * H))   # the two maps are inverse
+
+
+def test_one_rank_is_identity():
+    x = np.arange(1 * 2 * 16 * 4 * 8, dtype=np.uint32).reshape(1, 2, 16, 4, 8)
+    np.testing.assert_array_equal(oracle.seq_to_head(x, 2, 16, 4, 8, 1), x)
+    np.testing.assert_array_equal(oracle.head_to_seq(x, 2, 16, 4, 8, 1), x)
+
+
+def test_batch_one_seq_buffer_is_global_layout():
+    # B = 1: rank-major [P, 1, L/P, H, d] is byte-identical to the global [1, L, H, d]
+    B, L, H, d, P = 1, 16, 4, 2, 4
+    g = np.arange(L * H * d, dtype=np.uint32).reshape(L, H, d)          # global [L, H, d]
+    seq = np.stack([g[r * (L // P):(r + 1) * (L // P)] for r in range(P)])[:, None]
+    assert np.array_equal(seq.reshape(-1), g.reshape(-1))
+    y = oracle.seq_to_head(seq, B, L, H, d, P)
+    for p in range(P):  # rank p holds all tokens of heads p*Hp..
+        np.testing.assert_array_equal(y[p, 0], g[:, p * (H // P):(p + 1) * (H // P)])
+
+
+def _read_grid(name):
+    grids, cur = {}, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("["):
+                cur = line.strip("[]")
+                grids[cur] = []
+            else:
+                grids[cur].append([int(v) for v in line.split()])
+    return {k: np.array(v) for k, v in grids.items()}
+
+
+def test_ownership_grid_golden():
+    grids = _read_grid("ownership_L8_H4_P2.txt")
+    L, H, P, B, d = 8, 4, 2, 1, 1
+    # each cell carries its own (token, head) code; the seq buffer is laid out
+    # by the token cut of the grid
+    code = lambda t, h: 100 * t + h  # noqa: E731
+    seq = np.zeros((P, B, L // P, H, d), dtype=np.int64)
+    for t in range(L):
+        for h in range(H):
+            r = grids["token_cut"][t, h]
+            seq[r, 0, t - r * (L // P), h, 0] = code(t, h)
+    head = oracle.seq_to_head(seq, B, L, H, d, P)
+    for t in range(L):
+        for h in range(H):
+            p = grids["head_cut"][t, h]
+            j = h - p * (H // P)
+            assert head[p, 0, t, j, 0] == code(t, h)
+    np.testing.assert_array_equal(oracle.head_to_seq(head, B, L, H, d, P), seq)
+
+
+def test_permutation_moves_bits_not_values():
+    # NaN payloads, infinities, -0, subnormals: every bit pattern must survive
+    specials = np.array([0x7FC1, 0xFFC3, 0x7F81, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x807F, 0x3F80],
+                        dtype=np.uint16)
+    B, L, H, d, P = 1, 8, 4, 8, 2
+    x = np.resize(specials, (P, B, L // P, H, d)).astype(np.uint16)
+    y = oracle.seq_to_head(x, B, L, H, d, P)
+    assert sorted(y.ravel().tolist()) == sorted(x.ravel().tolist())
+    np.testing.assert_array_equal(oracle.head_to_seq(y, B, L, H, d, P), x)
+
+
+def test_divisibility_is_enforced():
+    with pytest.raises(ValueError):
+        oracle.seq_to_head_source_rows(1, 16, 6, 4)   # H % P != 0
+    with pytest.raises(ValueError):
+        oracle.seq_to_head_source_rows(1, 10, 4, 4)   # L % P != 0
+
+
+# ---------------------------------------------------------------------------
+# the bf16 encoding of inputs
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_known_patterns():
+    got = oracle.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x0001, 0x7F80, 0x8000, 0x4049], np.uint16))
+    assert got[0] == 1.0 and got[1] == -2.0 and got[2] == 2.0 ** -133
+    assert math.isinf(got[3]) and got[4] == 0.0 and math.copysign(1, got[4]) < 0
+    assert got[5] == 3.140625
+
+
+def test_bf16_round_to_nearest_even():
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -1.0 - 2.0 ** -8], np.float32)
+    got = oracle.bf16_bits_to_f64(f32_to_bf16_bits(x))
+    np.testing.assert_array_equal(got, [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -1.0])
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    y = (rng.standard_normal(100000) * 10.0 ** rng.uniform(-30, 30, 100000)).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(f32_to_bf16_bits(y), ref)
+
+
+# ---------------------------------------------------------------------------
+# attention forward
+# ---------------------------------------------------------------------------
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_zero_queries_or_keys_give_uniform_attention(causal):
+    B, L, Hh, d = 2, 37, 2, 8
+    v = _rand((B, L, Hh, d), 4)
+    nvis = np.arange(1, L + 1) if causal else np.full(L, L)
+    want = (np.cumsum(v, axis=1) / nvis[None, :, None, None]) if causal else np.broadcast_to(v.mean(axis=1, keepdims=True), v.shape)
+    for zero in ("q", "k"):
+        q = np.zeros((B, L, Hh, d)) if zero == "q" else _rand((B, L, Hh, d), 5)
+        k = np.zeros((B, L, Hh, d)) if zero == "k" else _rand((B, L, Hh, d), 6)
+        o, lse = oracle.attn_fwd(q, k, v, causal, row_block=16)
+        np.testing.assert_allclose(o, want, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, np.broadcast_to(np.log(nvis), lse.shape), rtol=0, atol=1e-13)
+
+
+def test_causal_row_zero_is_v0():
+    q, k, v = (_rand((1, 50, 3, 16), s) for s in (7, 8, 9))
+    o, lse = oracle.attn_fwd(q, k, v, True)
+    np.testing.assert_array_equal(o[:, 0], v[:, 0])
+    np.testing.assert_allclose(lse[:, :, 0], np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0]) / 4.0, rtol=1e-14)
+
+
+def test_two_token_closed_form():
+    # row 1 of a causal 2-token head: weights 1/(1+e^a), e^a/(1+e^a), a = (s11 - s10)
+    d = 4
+    q = np.array([[0.3, -0.2, 0.5, 0.1], [1.0, 2.0, -1.0, 0.5]])
+    k = np.array([[0.7, 0.1, -0.4, 0.2], [-0.3, 0.9, 0.8, -1.1]])
+    v = np.array([[1.0, 2.0, 3.0, 4.0], [-5.0, 6.0, -7.0, 8.0]])
+    s10 = sum(q[1, e] * k[0, e] for e in range(d)) / 2.0
+    s11 = sum(q[1, e] * k[1, e] for e in range(d)) / 2.0
+    a = math.exp(s11 - s10)
+    want = (v[0] + a * v[1]) / (1.0 + a)
+    o, lse = oracle.attn_fwd_head(q, k, v, True)
+    np.testing.assert_allclose(o[1], want, rtol=1e-14)
+    np.testing.assert_allclose(lse[1], s10 + math.log(1.0 + a), rtol=1e-14)
+
+
+def _brute_force_attention(q, k, v, causal):
+    """Pure-Python loops with math.exp: softmax of scaled dot products, then the weighted sum."""
+    L, d = len(q), len(q[0])
+    out, lses = [], []
+    for i in range(L):
+        js = range(i + 1) if causal else range(L)
+        s = [sum(q[i][e] * k[j][e] for e in range(d)) / math.sqrt(d) for j in js]
+        w = [math.exp(x) for x in s]
+        z = sum(w)
+        out.append([sum(w[n] * v[j][e] for n, j in enumerate(js)) / z for e in range(d)])
+        lses.append(math.log(z))
+    return np.array(out), np.array(lses)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_brute_force(causal):
+    q, k, v = (_rand((13, 5), s) for s in (10, 11, 12))
+    o, lse = oracle.attn_fwd_head(q, k, v, causal, row_block=4)
+    bo, blse = _brute_force_attention(q.tolist(), k.tolist(), v.tolist(), causal)
+    np.testing.assert_allclose(o, bo, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, blse, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_matches_torch_sdpa_fp64(causal):
+    torch = pytest.importorskip("torch")
+    B, L, Hh, d = 2, 300, 2, 64
+    q, k, v = (_rand((B, L, Hh, d), s, 2.0) for s in (13, 14, 15))
+    o, lse = oracle.attn_fwd(q, k, v, causal, row_block=64)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))  # noqa: E731
+    ref = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal)
+    np.testing.assert_allclose(o, ref.numpy().transpose(0, 2, 1, 3), rtol=0, atol=1e-12)
+    s = torch.einsum("bhid,bhjd->bhij", t(q), t(k)) / math.sqrt(d)
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-11)
+
+
+def test_softmax_invariants():
+    B, L, Hh, d = 1, 96, 2, 16
+    q, k, v = (_rand((B, L, Hh, d), s) for s in (16, 17, 18))
+    o, lse = oracle.attn_fwd(q, k, v, True, row_block=32)
+    # rows sum to one: V == 1 gives O == 1
+    o1, _ = oracle.attn_fwd(q, k, np.ones_like(v), True)
+    np.testing.assert_allclose(o1, 1.0, rtol=0, atol=1e-14)
+    # affine in V
+    oa, _ = oracle.attn_fwd(q, k, 3.0 * v - 2.0, True)
+    np.testing.assert_allclose(oa, 3.0 * o - 2.0, rtol=0, atol=1e-12)
+    # adding one vector c to every key shifts each row's scores by a constant
+    c = _rand((1, 1, Hh, d), 19)
+    ok, lsek = oracle.attn_fwd(q, k + c, v, True)
+    np.testing.assert_allclose(ok, o, rtol=0, atol=1e-12)
+    shift = np.einsum("blhd,bhd->bhl", q, c[:, 0]) / math.sqrt(d)
+    np.testing.assert_allclose(lsek, lse + shift, rtol=0, atol=1e-12)
+    # causal prefix: the first L' rows do not depend on later tokens
+    op, lsep = oracle.attn_fwd(q[:, :40], k[:, :40], v[:, :40], True)
+    np.testing.assert_allclose(op, o[:, :40], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lsep, lse[:, :, :40], rtol=0, atol=1e-14)
+
+
+def test_large_logits_stay_finite():
+    # rows scaled by 8 (the stress rows of the 30B-shaped workload) give logits in the hundreds
+    q = _rand((64, 128), 20, 0.5 * 8)
+    k = _rand((64, 128), 21, 0.5 * 8)
+    v = _rand((64, 128), 22)
+    o, lse = oracle.attn_fwd_head(q, k, v, True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    bo, blse = _brute_force_attention((q / 4).tolist(), (k * 4).tolist(), v.tolist(), True)
+    np.testing.assert_allclose(o, bo, rtol=1e-9, atol=1e-12)
+
+
+def test_pipeline_equals_monolithic():
+    # "numerically identical to monolithic attention" (aifetchly blog, simulator section)
+    B, L, H, d, P = 2, 64, 8, 16, 4
+    q, k, v = (_rand((P, B, L // P, H, d), s) for s in (23, 24, 25))
+    o_u, lse_u = oracle.ulysses_attention_fwd(q, k, v, B, L, H, d, P, True)
+    o_m = oracle.monolithic_attention_fwd(q, k, v, B, L, H, d, P, True)
+    np.testing.assert_array_equal(o_u, o_m)
+
+
+# ---------------------------------------------------------------------------
+# attention backward
+# ---------------------------------------------------------------------------
+
+def _objective(q, k, v, do, causal):
+    o, _ = oracle.attn_fwd(q, k, v, causal)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_finite_differences(causal):
+    B, L, Hh, d = 1, 12, 1, 6
+    q, k, v, do = (_rand((B, L, Hh, d), s) for s in (26, 27, 28, 29))
+    dq, dk, dv, o, lse, D = oracle.attn_bwd(q, k, v, do, causal, row_block=5)
+    h = 1e-5
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(grad.shape):
+            args = {"q": q.copy(), "k": k.copy(), "v": v.copy()}
+            args[name][idx] += h
+            fp = _objective(args["q"], args["k"], args["v"], do, causal)
+            args[name][idx] -= 2 * h
+            fm = _objective(args["q"], args["k"], args["v"], do, causal)
+            num[idx] = (fp - fm) / (2 * h)
+        err = np.max(np.abs(num - grad)) / np.max(np.abs(grad))
+        assert err < 1e-8, (name, err)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_matches_torch_autograd_fp64(causal):
+    torch = pytest.importorskip("torch")
+    B, L, Hh, d = 1, 200, 2, 32
+    q, k, v, do = (_rand((B, L, Hh, d), s) for s in (30, 31, 32, 33))
+    dq, dk, dv, o, lse, D = oracle.attn_bwd(q, k, v, do, causal, row_block=48)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).requires_grad_(True)  # noqa: E731
+    tq, tk, tv = t(q), t(k), t(v)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    out.backward(torch.from_numpy(np.ascontiguousarray(do.transpose(0, 2, 1, 3))))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy().transpose(0, 2, 1, 3), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(o, out.detach().numpy().transpose(0, 2, 1, 3), rtol=0, atol=1e-12)
+
+
+def test_backward_invariants_and_closed_forms():
+    B, L, Hh, d = 1, 70, 2, 8
+    q, k, v, do = (_rand((B, L, Hh, d), s) for s in (34, 35, 36, 37))
+    dq, dk, dv, o, lse, D = oracle.attn_bwd(q, k, v, do, True, row_block=32)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)           # rows of dS sum to zero
+    np.testing.assert_allclose(dv.sum(axis=1), do.sum(axis=1), atol=1e-12)  # rows of P sum to one
+    np.testing.assert_allclose(dq[:, 0], 0.0, atol=1e-14)                   # one visible key at row 0
+    np.testing.assert_allclose(D, np.einsum("blhd,blhd->bhl", do, o), atol=1e-13)
+    # Q = 0: uniform weights 1/(i+1); dK = 0; dV_j = sum_{i >= j} dO_i / (i+1)
+    z = np.zeros_like(q)
+    dq0, dk0, dv0, *_ = oracle.attn_bwd(z, k, v, do, True)
+    np.testing.assert_allclose(dk0, 0.0, atol=1e-14)
+    w = do / np.arange(1, L + 1)[None, :, None, None]
+    want = np.flip(np.cumsum(np.flip(w, axis=1), axis=1), axis=1)
+    np.testing.assert_allclose(dv0, want, atol=1e-13)
+    # linear in dO; dO = 0 gives zero gradients
+    dq2, dk2, dv2, *_ = oracle.attn_bwd(q, k, v, -2.5 * do, True)
+    np.testing.assert_allclose(dq2, -2.5 * dq, atol=1e-12)
+    np.testing.assert_allclose(dk2, -2.5 * dk, atol=1e-12)
+    np.testing.assert_allclose(dv2, -2.5 * dv, atol=1e-12)
+    dqz, dkz, dvz, *_ = oracle.attn_bwd(q, k, v, np.zeros_like(do), True)
+    assert not dqz.any() and not dkz.any() and not dvz.any()
+
+
+# ---------------------------------------------------------------------------
+# sampled evaluation agrees with the full oracle
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sampled_rows_and_columns(causal):
+    L, d = 150, 16
+    q, k, v, do = (_rand((L, d), s) for s in (38, 39, 40, 41))
+    dq, dk, dv, o, lse, D = oracle.attn_bwd_head(q, k, v, do, causal, row_block=32)
+    rows = [0, 1, 63, 64, 149]
+    r = oracle.attn_rows(q, k, v, rows, causal, do=do)
+    np.testing.assert_allclose(r["o"], o[rows], atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lse[rows], atol=1e-13)
+    np.testing.assert_allclose(r["dq"], dq[rows], atol=1e-12)
+    np.testing.assert_allclose(r["D"], D[rows], atol=1e-12)
+    cols, dkc, dvc = oracle.attn_dkv_cols(q, k, v, do, [149, 0, 77, 140, 31], causal, row_block=32)
+    np.testing.assert_allclose(dkc, dk[cols], atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the seeded inputs
+# ---------------------------------------------------------------------------
+
+def test_host_inputs_are_seeded_and_shaped():
+    wl = WORKLOADS["tiny-fp32-L256"]
+    a = host_tensor(wl, "q")
+    assert a.shape == (4, 1, 64, 8, 64) and a.dtype == np.float32
+    np.testing.assert_array_equal(a, host_tensor(wl, "q"))
+    assert not np.array_equal(a, host_tensor(wl, "k"))
+    assert abs(float(a.std()) - 1.0) < 0.02
+    wl2 = custom(1, 64, 4, 16, 2, dtype="bf16", stress_rows=True)
+    b = host_tensor(wl2, "q")
+    assert b.dtype == np.uint16 and b.shape == (2, 1, 32, 4, 16)
+    from workloads import stress_positions
+    pos = stress_positions(wl2, "q")
+    vals = oracle.bf16_bits_to_f64(b)
+    for h in range(4):
+        t = int(pos[0, h])
+        row = np.abs(vals[t // 32, 0, t % 32, h]).mean()
+        assert row > 4 * 0.5 * 0.5  # scaled by 8 from 0.5*N(0,1)
