@@ -1,0 +1,209 @@
+"""Benchmark of the Ulysses per-rank hot path on one MI355X.
+
+One step = the whole path over one batch of seeded synthetic input, inputs
+already resident in HBM:
+    seq_to_head on Q, K, V (and dO)          -- full [P][B][L/P][H][d_h] tensors
+    attention forward on rank 0's head group  -- [B][L][H/P][d_h], causal
+    attention backward (workloads with a backward pass)
+    head_to_seq on O (and dQ, dK, dV)         -- full head buffers
+Prints ONE JSON line. `value` is attention fwd(+bwd) algorithmic TFLOP/s over
+the whole step time (transposes included); per-op figures come from HIP
+events recorded on the launch stream around every call in the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s (% MFMA peak) + seq<->head transpose GB/s, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def npairs(L: int, causal: bool) -> int:
+    return L * (L + 1) // 2 if causal else L * L
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=12288,
+                    help="prefix length of one head that the fp64 oracle runs fwd+bwd on")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, seq_host, tokens: int):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    B, L, H, d, P = wl.B, wl.L, wl.H, wl.d, wl.P
+    Ls = min(tokens, L)
+    t0 = time.perf_counter()
+    heads = {n: oracle.seq_to_head_part(seq_host[n], B, L, H, d, P, 0) for n in seq_host}
+    t_perm = time.perf_counter() - t0
+    perm_bytes = 2 * sum(a.nbytes for a in seq_host.values()) // P   # one destination rank's share, read + write
+    f = {n: oracle.to_f64(heads[n][0, :Ls, 0], wl.dtype) for n in heads}
+    t0 = time.perf_counter()
+    if wl.backward:
+        oracle.attn_bwd_head(f["q"], f["k"], f["v"], f["do"], wl.causal)
+        flops = 14 * d * npairs(Ls, wl.causal)
+    else:
+        oracle.attn_fwd_head(f["q"], f["k"], f["v"], wl.causal)
+        flops = 4 * d * npairs(Ls, wl.causal)
+    t_attn = time.perf_counter() - t0
+    return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": threads if threads else cores,
+            "host_cores_visible": cores, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, {'fwd+bwd' if wl.backward else 'fwd'} of head 0 of rank 0 over the "
+                       f"first {Ls} tokens of the same inputs ({t_attn:.1f} s); flops counted as on the GPU"),
+            "perm_GBps": perm_bytes / t_perm / 1e9,
+            "perm_sample": f"seq_to_head of rank 0's share of {len(seq_host)} tensors ({t_perm:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU exchange is not "
+              "part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import exact_attention_ulysses_amd as U
+    from workloads import HEADLINE, WORKLOADS, device_tensor
+
+    wl = WORKLOADS[args.workload or HEADLINE]
+    B, L, H, d, P, Hh, causal = wl.B, wl.L, wl.H, wl.d, wl.P, wl.Hp, wl.causal
+    assert wl.dtype == "bf16", "bench.py measures the bf16 path"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    U.lib()
+
+    ins = ["q", "k", "v"] + (["do"] if wl.backward else [])
+    outs = ["o"] + (["dq", "dk", "dv"] if wl.backward else [])
+    seq = {n: device_tensor(wl, n, dev) for n in ins}
+    head = {n: torch.empty(wl.head_shape, dtype=torch.bfloat16, device=dev) for n in ins}
+    # output head buffers: rank 0's block is written by attention, the other blocks hold seeded filler
+    ohead = {n: device_tensor(wl, "fill_" + n, dev) for n in outs}
+    oseq = {n: torch.empty(wl.seq_shape, dtype=torch.bfloat16, device=dev) for n in outs}
+    lse = torch.empty((B, Hh, L), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, U.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, causal)), dtype=torch.uint8,
+                     device=dev)
+    r0 = {n: head[n][0] for n in ins}
+    o0 = {n: ohead[n][0] for n in outs}
+    stream = torch.cuda.current_stream()
+
+    ops = []  # (name, callable)
+    for n in ins:
+        ops.append(("seq_to_head", lambda n=n: U.ulysses_seq_to_head(seq[n], head[n], B, L, H, d, P)))
+    ops.append(("attn_fwd", lambda: U.ulysses_attn_fwd(r0["q"], r0["k"], r0["v"], o0["o"], lse, B, L, H, d, P,
+                                                       causal)))
+    if wl.backward:
+        ops.append(("attn_bwd", lambda: U.ulysses_attn_bwd(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], lse,
+                                                           o0["dq"], o0["dk"], o0["dv"], ws, B, L, H, d, P,
+                                                           causal)))
+    for n in outs:
+        ops.append(("head_to_seq", lambda n=n: U.ulysses_head_to_seq(ohead[n], oseq[n], B, L, H, d, P)))
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    per_op = {}
+    for s in range(args.steps):
+        for i, (name, _) in enumerate(ops):
+            per_op.setdefault(name, []).append(evs[s][i][0].elapsed_time(evs[s][i][1]))
+    avg = {k: sum(v) / len(v) for k, v in per_op.items()}       # ms per launch of that op
+    calls = {k: len(v) // args.steps for k, v in per_op.items()}
+
+    npr = npairs(L, causal)
+    fwd_flops = 4 * d * npr * B * Hh
+    bwd_flops = 10 * d * npr * B * Hh
+    attn_flops = fwd_flops + (bwd_flops if wl.backward else 0)
+    tensor_bytes = B * L * H * d * 2
+    perm_ms = avg["seq_to_head"] * calls["seq_to_head"] + avg["head_to_seq"] * calls["head_to_seq"]
+    perm_bytes = 2 * tensor_bytes * (calls["seq_to_head"] + calls["head_to_seq"])
+    attn_ms = avg["attn_fwd"] + (avg.get("attn_bwd", 0.0))
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+
+    # dominant op: largest share of the step
+    dom = max(("attn_fwd", "attn_bwd") if wl.backward else ("attn_fwd",), key=lambda k: avg[k])
+    dom_flops = bwd_flops if dom == "attn_bwd" else fwd_flops
+    achieved = dom_flops / (avg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": ("ulysses_attn_bwd (delta, dK/dV and dQ launches)" if dom == "attn_bwd"
+                                            else "ulysses_attn_fwd"),
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch": {"flops": dom_flops, "ms": avg[dom]}}
+
+    detail = {
+        "attn_fwd_ms": avg["attn_fwd"], "attn_fwd_TFLOPs": fwd_flops / (avg["attn_fwd"] * 1e-3) / 1e12,
+        "attn_fwd_bwd_TFLOPs": attn_flops / (attn_ms * 1e-3) / 1e12,
+        "attn_fwd_bwd_frac_peak": attn_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attn_12dN_TFLOPs": (12 if wl.backward else 4) * d * npr * B * Hh / (attn_ms * 1e-3) / 1e12,
+        "seq_to_head_ms": avg["seq_to_head"], "head_to_seq_ms": avg["head_to_seq"],
+        "transpose_GBps": perm_bytes / (perm_ms * 1e-3) / 1e9,
+        "transpose_frac_peak": perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "wall_s_timed_region": wall,
+    }
+    if wl.backward:
+        detail.update({"attn_bwd_ms": avg["attn_bwd"],
+                       "attn_bwd_TFLOPs": bwd_flops / (avg["attn_bwd"] * 1e-3) / 1e12})
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        host = {n: seq[n].view(torch.int16).cpu().numpy().view("uint16") for n in ins}
+        cpu = cpu_baseline(wl, host, args.cpu_sample_tokens)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, device-generated)",
+        "config": {"workload": wl.key, "B": B, "L": L, "H": H, "d_h": d, "P": P, "local_heads": Hh,
+                   "causal": causal, "backward": wl.backward, "parallelism": "1 GPU, P virtual ranks"},
+        "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

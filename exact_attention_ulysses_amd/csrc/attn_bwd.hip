@@ -1,0 +1,506 @@
+// Exact attention backward on one rank's head group.
+//
+// The pages train with the method but leave its backward implicit; this is
+// the exact gradient of softmax(Q K^T / sqrt(d_h)) V. The probabilities are
+// not stored by the forward pass (the N x N matrix is never materialised,
+// paper-graph summary of arXiv 2309.14509, section 3.4.5 on FlashAttention);
+// they are recomputed from the saved log-sum-exp: P_ij = exp(S_ij - lse_i).
+//   delta_i = sum_e dO_ie O_ie                  (preprocess kernel)
+//   dV = P^T dO, dS = P o (dO V^T - delta)        (dK/dV kernel)
+//   dK = dS^T Q / sqrt(d_h)                       (dK/dV kernel)
+//   dQ = dS K / sqrt(d_h)                         (dQ kernel)
+// dK/dV and dQ are produced by two kernels that each own their output rows,
+// so every output element is written once, without atomics, and results are
+// bitwise reproducible; the price is that S and dP are formed twice.
+//
+// bf16 dK/dV kernel: workgroup = 4 waves x 32 key rows; K and V of a wave's
+//   keys stay in registers; query tiles of 64 rows (Q, dO, lse, delta) are
+//   staged through LDS. S = Q K^T and dP = dO V^T put keys across lanes, so
+//   the accumulators become the B operands of dV^T += dO^T P and
+//   dK^T += Q^T dS directly; dO^T and Q^T are read transposed from LDS.
+// bf16 dQ kernel: workgroup = 4 waves x 32 query rows; the forward kernel's
+//   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "mfma_frag.h"
+
+namespace ulysses {
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// delta[b][h][i] = sum_e dO[b][i][h][e] * O[b][i][h][e]; D/8 lanes per row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o, const T* __restrict__ d_o,
+                                                        float* __restrict__ delta, int L, int Hh, int rows) {
+  constexpr int G = D / 8;
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  const int r = gt / G, part = gt % G;
+  float acc = 0.f;
+  if (r < rows) {
+    const T* po = o + (size_t)r * D + part * 8;
+    const T* pd = d_o + (size_t)r * D + part * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf((float)po[i], (float)pd[i], acc);
+  }
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (r < rows && part == 0) {
+    const int h = r % Hh;
+    const int bl = r / Hh;
+    const int b = bl / L, i = bl - b * L;
+    delta[((size_t)b * Hh + h) * L + i] = acc;
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, int Hh, int nhb, float sl2, float scale) {
+  constexpr int BQ = 64, ST = D + 8, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256;
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[BQ * ST];
+  __shared__ __attribute__((aligned(16))) __bf16 Ds[BQ * ST];   // dO tile
+  __shared__ __attribute__((aligned(16))) float lse2s[BQ];
+  __shared__ __attribute__((aligned(16))) float dls[BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int kb = blockIdx.x / nhb;  // key block 0 has the most query tiles under the causal mask
+  const int hb = blockIdx.x % nhb;
+  const int b = hb / Hh, h = hb - b * Hh;
+  const size_t rs = (size_t)Hh * D;
+  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const __bf16* qh = q + head_off;
+  const __bf16* doh = d_o + head_off;
+  const float* lseh = lse + (size_t)hb * L;
+  const float* dlh = delta + (size_t)hb * L;
+  const int k0w = kb * 128 + 32 * wave;
+  const int key = k0w + l32;
+
+  // K and V rows of this lane's key as B operands (k = head dim)
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (key < L) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(k + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(v + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
+    } else {
+      kf[ks] = bf16x8{};
+      vf[ks] = bf16x8{};
+    }
+  }
+  f32x16 dkacc[DT], dvacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dkacc[dt] = f32x16{};
+    dvacc[dt] = f32x16{};
+  }
+
+  const int qstart = CAUSAL ? kb * 128 : 0;
+  const int nqt = (L - qstart + BQ - 1) / BQ;
+  u32x4 qreg[CH], dreg[CH];
+  float lse_r = 0.f, dl_r = 0.f;
+  auto load_tile = [&](int qt) {
+    const int q0 = qstart + qt * BQ;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      const int qi = q0 + row;
+      if (qi < L) {
+        qreg[j] = *reinterpret_cast<const u32x4*>(qh + (size_t)qi * rs + col);
+        dreg[j] = *reinterpret_cast<const u32x4*>(doh + (size_t)qi * rs + col);
+      } else {
+        qreg[j] = u32x4{0, 0, 0, 0};
+        dreg[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int qi = q0 + tid;
+      // rows past the end get lse = +inf, so their probabilities are exactly 0
+      lse_r = qi < L ? lseh[qi] * kLog2e : INFINITY;
+      dl_r = qi < L ? dlh[qi] : 0.f;
+    }
+  };
+
+  load_tile(0);
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int q0 = qstart + qt * BQ;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      *reinterpret_cast<u32x4*>(Qs + row * ST + col) = qreg[j];
+      *reinterpret_cast<u32x4*>(Ds + row * ST + col) = dreg[j];
+    }
+    if (tid < BQ) {
+      lse2s[tid] = lse_r;
+      dls[tid] = dl_r;
+    }
+    __syncthreads();
+    if (qt + 1 < nqt) load_tile(qt + 1);
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma32(frag_row<ST>(Qs, 32 * u, 16 * ks, lane), kf[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32(frag_row<ST>(Ds, 32 * u, 16 * ks, lane), vf[ks], dp);
+      const bool need_mask = CAUSAL && (k0w + 31 > q0 + 32 * u);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r0 = 32 * u + 8 * a + 4 * hl;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + r0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * a + i;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -l4[i]));
+          if (need_mask && key > q0 + r0 + i) p = 0.f;
+          s[e] = p;
+          dp[e] = p * (dp[e] - d4[i]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pf = acc_chunk_bf16(s, c);
+        const bf16x8 dsf = acc_chunk_bf16(dp, c);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dvacc[dt] = mfma32(frag_col<ST>(Ds, 32 * u + 16 * c, 32 * dt, lane), pf, dvacc[dt]);
+          dkacc[dt] = mfma32(frag_col<ST>(Qs, 32 * u + 16 * c, 32 * dt, lane), dsf, dkacc[dt]);
+        }
+      }
+    }
+  }
+
+  if (key < L) {
+    __bf16* dkrow = dk + head_off + (size_t)key * rs;
+    __bf16* dvrow = dv + head_off + (size_t)key * rs;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        *reinterpret_cast<bf16x4*>(dkrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dkacc[dt], a, scale);
+        *reinterpret_cast<bf16x4*>(dvrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dvacc[dt], a, 1.f);
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dq, int L, int Hh, int nqb, int nhb, float sl2, float scale) {
+  constexpr int BM = 128, BN = 64, ST = D + 8, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * ST];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[BN * ST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int qb = nqb - 1 - (int)blockIdx.x / nhb;
+  const int hb = blockIdx.x % nhb;
+  const int b = hb / Hh, h = hb - b * Hh;
+  const size_t rs = (size_t)Hh * D;
+  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const __bf16* kh = k + head_off;
+  const __bf16* vh = v + head_off;
+  const int q0 = qb * BM;
+  const int qrow = q0 + 32 * wave + l32;
+  const bool valid = qrow < L;
+
+  bf16x8 qf[KS], df[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (valid) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q + head_off + (size_t)qrow * rs + 16 * ks + 8 * hl);
+      df[ks] = *reinterpret_cast<const bf16x8*>(d_o + head_off + (size_t)qrow * rs + 16 * ks + 8 * hl);
+    } else {
+      qf[ks] = bf16x8{};
+      df[ks] = bf16x8{};
+    }
+  }
+  const float lse2 = valid ? lse[(size_t)hb * L + qrow] * kLog2e : 0.f;
+  const float dl = valid ? delta[(size_t)hb * L + qrow] : 0.f;
+
+  f32x16 dqacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqacc[dt] = f32x16{};
+
+  const int kend = CAUSAL ? min(L, q0 + BM) : L;
+  const int nkb = (kend + BN - 1) / BN;
+  u32x4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      const int kk = kb * BN + row;
+      if (kk < L) {
+        kreg[j] = *reinterpret_cast<const u32x4*>(kh + (size_t)kk * rs + col);
+        vreg[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)kk * rs + col);
+      } else {
+        kreg[j] = u32x4{0, 0, 0, 0};
+        vreg[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  load_tile(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      *reinterpret_cast<u32x4*>(Ks + row * ST + col) = kreg[j];
+      *reinterpret_cast<u32x4*>(Vs + row * ST + col) = vreg[j];
+    }
+    __syncthreads();
+    if (kb + 1 < nkb) load_tile(kb + 1);
+    const int k0 = kb * BN;
+    const bool need_mask = CAUSAL ? (k0 + BN - 1 > q0 + 32 * wave) : (k0 + BN > L);
+
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma32(frag_row<ST>(Ks, 32 * mt, 16 * ks, lane), qf[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dp = mfma32(frag_row<ST>(Vs, 32 * mt, 16 * ks, lane), df[ks], dp);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lse2));
+        if (need_mask) {
+          const int kk = k0 + 32 * mt + 8 * (e >> 2) + 4 * hl + (e & 3);
+          if (CAUSAL ? (kk > qrow) : (kk >= L)) p = 0.f;
+        }
+        s[e] = p * (dp[e] - dl);  // dS^T of this 32-key sub-tile
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 dsf = acc_chunk_bf16(s, c);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          dqacc[dt] = mfma32(frag_col<ST>(Ks, 32 * mt + 16 * c, 32 * dt, lane), dsf, dqacc[dt]);
+      }
+    }
+  }
+
+  if (valid) {
+    __bf16* row = dq + head_off + (size_t)qrow * rs;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<bf16x4*>(row + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dqacc[dt], a, scale);
+    }
+  }
+}
+
+// fp32 dK/dV: one lane per key row.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dk, float* __restrict__ dv, int L, int Hh, int nhb, float scale) {
+  constexpr int BQ = 32;
+  __shared__ float Qs[BQ][D];
+  __shared__ float Os[BQ][D];
+  __shared__ float ls[BQ], dls[BQ];
+  const int tid = threadIdx.x;
+  const int kb = blockIdx.x / nhb;
+  const int hb = blockIdx.x % nhb;
+  const int b = hb / Hh, h = hb - b * Hh;
+  const size_t rs = (size_t)Hh * D;
+  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const int key = kb * 64 + tid;
+  const bool valid = key < L;
+  float kv[D], vv[D], dka[D], dva[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    kv[e] = valid ? k[head_off + (size_t)key * rs + e] : 0.f;
+    vv[e] = valid ? v[head_off + (size_t)key * rs + e] : 0.f;
+    dka[e] = 0.f;
+    dva[e] = 0.f;
+  }
+  const int qstart = CAUSAL ? kb * 64 : 0;
+  for (int q0 = qstart; q0 < L; q0 += BQ) {
+    __syncthreads();
+    for (int c = tid; c < BQ * D; c += 64) {
+      const int r = c / D, e = c % D, qi = q0 + r;
+      Qs[r][e] = qi < L ? q[head_off + (size_t)qi * rs + e] : 0.f;
+      Os[r][e] = qi < L ? d_o[head_off + (size_t)qi * rs + e] : 0.f;
+    }
+    if (tid < BQ) {
+      const int qi = q0 + tid;
+      ls[tid] = qi < L ? lse[(size_t)hb * L + qi] : 0.f;
+      dls[tid] = qi < L ? delta[(size_t)hb * L + qi] : 0.f;
+    }
+    __syncthreads();
+    const int rn = min(BQ, L - q0);
+    for (int r = 0; r < rn; ++r) {
+      if (CAUSAL && q0 + r < key) continue;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        s = fmaf(Qs[r][e], kv[e], s);
+        dp = fmaf(Os[r][e], vv[e], dp);
+      }
+      const float p = expf(s * scale - ls[r]);
+      const float ds = p * (dp - dls[r]);
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        dva[e] = fmaf(p, Os[r][e], dva[e]);
+        dka[e] = fmaf(ds, Qs[r][e], dka[e]);
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      dk[head_off + (size_t)key * rs + e] = dka[e] * scale;
+      dv[head_off + (size_t)key * rs + e] = dva[e];
+    }
+  }
+}
+
+// fp32 dQ: one lane per query row.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dq, int L, int Hh, int nqb, int nhb, float scale) {
+  constexpr int BN = 32;
+  __shared__ float Ks[BN][D];
+  __shared__ float Vs[BN][D];
+  const int tid = threadIdx.x;
+  const int qb = nqb - 1 - (int)blockIdx.x / nhb;
+  const int hb = blockIdx.x % nhb;
+  const int b = hb / Hh, h = hb - b * Hh;
+  const size_t rs = (size_t)Hh * D;
+  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const int qrow = qb * 64 + tid;
+  const bool valid = qrow < L;
+  float qv[D], dov[D], dqa[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = valid ? q[head_off + (size_t)qrow * rs + e] : 0.f;
+    dov[e] = valid ? d_o[head_off + (size_t)qrow * rs + e] : 0.f;
+    dqa[e] = 0.f;
+  }
+  const float l_i = valid ? lse[(size_t)hb * L + qrow] : 0.f;
+  const float d_i = valid ? delta[(size_t)hb * L + qrow] : 0.f;
+  const int kend = CAUSAL ? min(L, qb * 64 + 64) : L;
+  for (int k0 = 0; k0 < kend; k0 += BN) {
+    __syncthreads();
+    for (int c = tid; c < BN * D; c += 64) {
+      const int r = c / D, e = c % D, kk = k0 + r;
+      Ks[r][e] = kk < L ? k[head_off + (size_t)kk * rs + e] : 0.f;
+      Vs[r][e] = kk < L ? v[head_off + (size_t)kk * rs + e] : 0.f;
+    }
+    __syncthreads();
+    const int jn = min(BN, L - k0);
+    for (int j = 0; j < jn; ++j) {
+      if (CAUSAL && k0 + j > qrow) break;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        s = fmaf(qv[e], Ks[j][e], s);
+        dp = fmaf(dov[e], Vs[j][e], dp);
+      }
+      const float p = expf(s * scale - l_i);
+      const float ds = p * (dp - d_i);
+#pragma unroll
+      for (int e = 0; e < D; ++e) dqa[e] = fmaf(ds, Ks[j][e], dqa[e]);
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < D; ++e) dq[head_off + (size_t)qrow * rs + e] = dqa[e] * scale;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_delta(const T* o, const T* d_o, float* delta, const AttnShape& s, hipStream_t stream) {
+  const int rows = s.B * s.L * s.Hh;
+  const long long threads = (long long)rows * (D / 8);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, o, d_o, delta, s.L, s.Hh, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                    void* dq, void* dk, void* dv, float* delta, const AttnShape& s, hipStream_t stream) {
+  hipError_t e = launch_delta<__bf16, D>((const __bf16*)o, (const __bf16*)d_o, delta, s, stream);
+  if (e != hipSuccess) return e;
+  const int nhb = s.B * s.Hh;
+  const float scale = 1.f / sqrtf((float)D);
+  const float sl2 = scale * kLog2e;
+  const int nkb = (s.L + 127) / 128;
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)nkb * nhb), dim3(256), 0, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                     (__bf16*)dk, (__bf16*)dv, s.L, s.Hh, nhb, sl2, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (s.L + 127) / 128;
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                     (__bf16*)dq, s.L, s.Hh, nqb, nhb, sl2, scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* d_o,
+                   const float* lse, float* dq, float* dk, float* dv, float* delta, const AttnShape& s,
+                   hipStream_t stream) {
+  hipError_t e = launch_delta<float, D>(o, d_o, delta, s, stream);
+  if (e != hipSuccess) return e;
+  const int nhb = s.B * s.Hh;
+  const float scale = 1.f / sqrtf((float)D);
+  const int nb = (s.L + 63) / 64;
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)nb * nhb), dim3(64), 0, stream, q, k, v, d_o,
+                     lse, delta, dk, dv, s.L, s.Hh, nhb, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)nb * nhb), dim3(64), 0, stream, q, k, v, d_o,
+                     lse, delta, dq, s.L, s.Hh, nb, nhb, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(const AttnShape& s) {
+  const size_t delta = (size_t)s.B * s.Hh * s.L * sizeof(float);
+  return (delta + 255) / 256 * 256;
+}
+
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                                const AttnShape& s, hipStream_t stream) {
+  float* delta = static_cast<float*>(workspace);
+  if (s.D == 128)
+    return s.causal ? bwd_bf16<128, true>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream)
+                    : bwd_bf16<128, false>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream);
+  return s.causal ? bwd_bf16<64, true>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream)
+                  : bwd_bf16<64, false>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream);
+}
+
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* d_o,
+                               const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                               const AttnShape& s, hipStream_t stream) {
+  float* delta = static_cast<float*>(workspace);
+  if (s.D == 128)
+    return s.causal ? bwd_f32<128, true>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream)
+                    : bwd_f32<128, false>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream);
+  return s.causal ? bwd_f32<64, true>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream)
+                  : bwd_f32<64, false>(q, k, v, o, d_o, lse, dq, dk, dv, delta, s, stream);
+}
+
+}  // namespace ulysses

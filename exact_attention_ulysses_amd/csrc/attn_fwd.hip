@@ -1,0 +1,272 @@
+// Exact attention forward on one rank's head group, full sequence.
+//
+// O = softmax(Q K^T / sqrt(d_h)) V per (batch, head), causal or not
+// (papers.chlience.com reading note, section 5.1; paper-graph summary of
+// arXiv 2309.14509, sections 3.2 and 3.4.5). The N x N score matrix is never
+// formed in memory (paper-graph summary, section 3.4.5, on FlashAttention):
+// each workgroup walks the key blocks of its query block with a running row
+// maximum and row sum, and writes the log-sum-exp of every row for the
+// backward pass.
+//
+// bf16 path (gfx950 MFMA, 32x32x16):
+//   workgroup = 4 waves x 32 query rows = 128 rows; key blocks of 64 rows.
+//   Each wave computes S^T = K Q^T for its rows (keys down the accumulator
+//   rows, queries across lanes), so a query's scores sit in one lane pair and
+//   the row max / sum need one cross-lane exchange. O^T = V^T P^T reuses the
+//   score registers as the B operand; V is read transposed from its row-major
+//   LDS tile with ds_read_b64_tr_b16. Q stays in registers for the whole key
+//   walk; the next K/V tile is loaded into registers while the current one is
+//   used from LDS. Causal query blocks are dispatched longest first and never
+//   visit key blocks above the diagonal.
+// fp32 path: one lane per query row, K/V tiles in LDS, plain FMAs (used for
+//   the small fp32 workloads; precision reference for the tests).
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "mfma_frag.h"
+
+namespace ulysses {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int L, int Hh, int nqb, int nhb, float sl2) {
+  constexpr int BM = 128, BN = 64, ST = D + 8, KS = D / 16, DT = D / 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int CH = BN * CPR / 256;         // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * ST];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[BN * ST];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int qb = nqb - 1 - bid / nhb;  // longest rows first
+  const int hb = bid % nhb;            // (batch, head) pair
+  const int b = hb / Hh, h = hb - b * Hh;
+  const size_t rs = (size_t)Hh * D;
+  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const __bf16* qh = q + head_off;
+  const __bf16* kh = k + head_off;
+  const __bf16* vh = v + head_off;
+  const int q0 = qb * BM;
+  const int qrow = q0 + 32 * wave + l32;
+
+  // Q^T as the B operand: lane holds Q[qrow][16 ks + 8 hl .. +7]
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qrow < L)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * rs + 16 * ks + 8 * hl);
+    else
+      qf[ks] = bf16x8{};
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = CAUSAL ? min(L, q0 + BM) : L;
+  const int nkb = (kend + BN - 1) / BN;
+
+  u32x4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      const int key = kb * BN + row;
+      if (key < L) {
+        kreg[j] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * rs + col);
+        vreg[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)key * rs + col);
+      } else {
+        kreg[j] = u32x4{0, 0, 0, 0};
+        vreg[j] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  load_tile(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c / CPR, col = (c % CPR) * 8;
+      *reinterpret_cast<u32x4*>(Ks + row * ST + col) = kreg[j];
+      *reinterpret_cast<u32x4*>(Vs + row * ST + col) = vreg[j];
+    }
+    __syncthreads();
+    if (kb + 1 < nkb) load_tile(kb + 1);
+    const int k0 = kb * BN;
+
+    // S^T = K Q^T: two 32-key sub-tiles
+    f32x16 s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[mt] = mfma32(frag_row<ST>(Ks, 32 * mt, 16 * ks, lane), qf[ks], s[mt]);
+    }
+
+    const bool need_mask = CAUSAL ? (k0 + BN - 1 > q0 + 32 * wave) : (k0 + BN > L);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = s[mt][e] * sl2;
+        if (need_mask) {
+          const int key = k0 + 32 * mt + 8 * (e >> 2) + 4 * hl + (e & 3);
+          if (CAUSAL ? (key > qrow) : (key >= L)) x = -INFINITY;
+        }
+        s[mt][e] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float rsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(s[mt][e] - m_new);
+        s[mt][e] = p;
+        rsum += p;
+      }
+    }
+    l_run = l_run * alpha + rsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+
+    // O^T += V^T P^T over four 16-key chunks
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf16x8 pf = acc_chunk_bf16(s[c >> 1], c & 1);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<ST>(Vs, 16 * c, 32 * dt, lane), pf, oacc[dt]);
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.f / l_tot;
+  if (qrow < L) {
+    __bf16* orow = o + head_off + (size_t)qrow * rs;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
+    }
+    if (hl == 0) lse[(size_t)hb * L + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// fp32: one lane per query row.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int L, int Hh, int nqb, int nhb, float scale) {
+  constexpr int BN = 32;
+  __shared__ float Ks[BN][D];
+  __shared__ float Vs[BN][D];
+  const int tid = threadIdx.x;
+  const int qb = nqb - 1 - (int)blockIdx.x / nhb;
+  const int hb = blockIdx.x % nhb;
+  const int b = hb / Hh, h = hb - b * Hh;
+  const size_t rs = (size_t)Hh * D;
+  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const int qrow = qb * 64 + tid;
+  const bool valid = qrow < L;
+
+  float qv[D], ov[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = valid ? q[head_off + (size_t)qrow * rs + e] * scale : 0.f;
+    ov[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = CAUSAL ? min(L, qb * 64 + 64) : L;
+  for (int k0 = 0; k0 < kend; k0 += BN) {
+    __syncthreads();
+    for (int c = tid; c < BN * D; c += 64) {
+      const int r = c / D, e = c % D, key = k0 + r;
+      Ks[r][e] = key < L ? k[head_off + (size_t)key * rs + e] : 0.f;
+      Vs[r][e] = key < L ? v[head_off + (size_t)key * rs + e] : 0.f;
+    }
+    __syncthreads();
+    const int jn = min(BN, L - k0);
+    for (int j = 0; j < jn; ++j) {
+      if (CAUSAL && k0 + j > qrow) break;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) s = fmaf(qv[e], Ks[j][e], s);
+      if (s > m) {
+        const float c = expf(m - s);
+        l *= c;
+#pragma unroll
+        for (int e = 0; e < D; ++e) ov[e] *= c;
+        m = s;
+      }
+      const float p = expf(s - m);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) ov[e] = fmaf(p, Vs[j][e], ov[e]);
+    }
+  }
+  if (valid) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[head_off + (size_t)qrow * rs + e] = ov[e] * inv;
+    lse[(size_t)hb * L + qrow] = m + logf(l);
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnShape& s,
+                    hipStream_t stream) {
+  const int nqb = (s.L + 127) / 128;
+  const int nhb = s.B * s.Hh;
+  const float sl2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.L, s.Hh, nqb,
+                     nhb, sl2);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, const AttnShape& s,
+                   hipStream_t stream) {
+  const int nqb = (s.L + 63) / 64;
+  const int nhb = s.B * s.Hh;
+  const float scale = 1.f / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(64), 0, stream, q, k, v,
+                     o, lse, s.L, s.Hh, nqb, nhb, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const AttnShape& s, hipStream_t stream) {
+  if (s.D == 128) return s.causal ? fwd_bf16<128, true>(q, k, v, o, lse, s, stream)
+                                  : fwd_bf16<128, false>(q, k, v, o, lse, s, stream);
+  return s.causal ? fwd_bf16<64, true>(q, k, v, o, lse, s, stream) : fwd_bf16<64, false>(q, k, v, o, lse, s, stream);
+}
+
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                               const AttnShape& s, hipStream_t stream) {
+  if (s.D == 128) return s.causal ? fwd_f32<128, true>(q, k, v, o, lse, s, stream)
+                                  : fwd_f32<128, false>(q, k, v, o, lse, s, stream);
+  return s.causal ? fwd_f32<64, true>(q, k, v, o, lse, s, stream) : fwd_f32<64, false>(q, k, v, o, lse, s, stream);
+}
+
+}  // namespace ulysses

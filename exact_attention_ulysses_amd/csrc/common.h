@@ -1,0 +1,51 @@
+// Internal helpers of the HIP library (gfx950 only). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ulysses {
+
+// ---------------------------------------------------------------------------
+// vector types for MFMA operands and wide memory access
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// division by a runtime constant without a hardware divide: q = n / d for
+// n < 2^32, with m = ceil(2^(32+s) / d) - 2^32 (Granlund & Montgomery 1994,
+// "Division by invariant integers using multiplication", round-up variant).
+// ---------------------------------------------------------------------------
+struct FastDiv {
+  uint32_t d;
+  uint32_t m;
+  uint32_t s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((uint64_t(1) << s) < d) ++s;
+  f.s = s;
+  f.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  uint32_t t = __umulhi(n, f.m);
+  return uint32_t((uint64_t(t) + n) >> f.s);
+}
+
+// ---------------------------------------------------------------------------
+// launch-side error reporting (thread-local last error text)
+// ---------------------------------------------------------------------------
+void set_last_hip_error(hipError_t e);
+
+}  // namespace ulysses

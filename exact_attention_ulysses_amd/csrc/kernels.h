@@ -1,0 +1,42 @@
+// Internal launcher declarations (validated arguments only). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ulysses {
+
+struct PermShape {
+  uint32_t P, B, Lp;       // ranks, batch, tokens per rank
+  uint32_t run_bytes;      // H/P * d_h * element size (multiple of 128)
+  uint32_t total_words;    // tensor size in 16-byte words (< 2^31)
+};
+
+hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, bool seq_to_head,
+                                hipStream_t stream);
+
+struct AttnShape {
+  int B;        // batch (times ranks when several head groups run at once)
+  int L;        // sequence length
+  int Hh;       // heads in the buffer (H/P)
+  int D;        // head dim (64 or 128)
+  bool causal;
+};
+
+// bf16 operands, fp32 lse
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const AttnShape& s, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                               const AttnShape& s, hipStream_t stream);
+
+// workspace layout: delta [B][Hh][L] fp32, then (256-byte aligned) nothing else
+size_t attn_bwd_workspace_bytes(const AttnShape& s);
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const void* d_o, const float* lse, void* dq, void* dk, void* dv,
+                                void* workspace, const AttnShape& s, hipStream_t stream);
+hipError_t launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                               const float* d_o, const float* lse, float* dq, float* dk, float* dv,
+                               void* workspace, const AttnShape& s, hipStream_t stream);
+
+}  // namespace ulysses

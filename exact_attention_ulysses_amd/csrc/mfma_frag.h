@@ -1,0 +1,68 @@
+// MFMA operand fetch for gfx950 v_mfma_f32_32x32x16_bf16 (internal).
+//
+// Register layouts of the instruction (64 lanes, l = lane):
+//   A (32 x 16, bf16x8): lane l holds A[l % 32][8 * (l / 32) + i], i = 0..7
+//   B (16 x 32, bf16x8): lane l holds B[8 * (l / 32) + i][l % 32]
+//   C (32 x 32, f32x16): lane l holds C[8 * (e / 4) + 4 * (l / 32) + e % 4][l % 32]
+// Only the pairing of A's and B's k slots matters to the product, so an
+// operand may enumerate its 16 k values in any order as long as the other
+// operand uses the same one. Tiles live row-major in LDS; an operand whose k
+// runs along a row is one 16-byte read per lane, an operand whose k runs down
+// a column uses two ds_read_b64_tr_b16 transposing reads and enumerates k in
+// the order in which a converted 32x32 accumulator holds its rows.
+#pragma once
+
+#include "common.h"
+
+namespace ulysses {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// k along a row: lane l gets T[row0 + l % 32][col0 + 8 * (l / 32) + i].
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 frag_row(const __bf16* t, int row0, int col0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(t + (row0 + (lane & 31)) * STRIDE + col0 + 8 * (lane >> 5));
+}
+
+// k down a column: lane l gets T[row0 + 8 * (i / 4) + 4 * (l / 32) + i % 4][col0 + l % 32].
+// ds_read_b64_tr_b16 hands lane j of each 16-lane group element j % 4 of the
+// 8-byte blocks addressed by lanes 4i + j / 4 of the group; so lane 4i + c
+// addresses row (its 4-row group) + i, columns 4c .. 4c + 3 of its 16-column half.
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 frag_col(const __bf16* t, int row0, int col0, int lane) {
+  const int j = lane & 15;
+  const int row = row0 + 4 * (lane >> 5) + (j >> 2);
+  const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  __bf16* p = const_cast<__bf16*>(t) + row * STRIDE + col;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * STRIDE));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// Elements 8c .. 8c+7 of a 32x32 accumulator, rounded to bf16, as an operand
+// whose k slots are accumulator rows 16c + 8 * (i / 4) + 4 * (l / 32) + i % 4:
+// the same k order frag_col produces for rows starting at 16c.
+__device__ __forceinline__ bf16x8 acc_chunk_bf16(const f32x16& a, int c) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)a[8 * c + i];
+  return r;
+}
+
+// Four consecutive accumulator elements 4a .. 4a+3 (rows 8a + 4 * (l / 32) + 0..3)
+// as bf16, for an 8-byte store.
+__device__ __forceinline__ bf16x4 acc_quad_bf16(const f32x16& a, int q, float scale) {
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (__bf16)(a[4 * q + i] * scale);
+  return r;
+}
+
+}  // namespace ulysses

@@ -1,0 +1,97 @@
+// seq <-> head layout change over P virtual ranks (the two all-to-alls of one
+// attention block, done as on-device permutations).
+//
+// "Ulysses Sequence Parallelism: A Temporary Change of Layout" (pinyu.ai),
+// section "Use the other independent axis": each sender cuts its heads into P
+// groups and each receiver concatenates the token blocks it gets in sender
+// order; paper-graph summary of arXiv 2309.14509, section 3.4.1: contiguous
+// token chunks before, contiguous head groups after.
+//
+// Both directions are one 5-D axis permutation whose innermost run is one
+// (token, head-group) slab of H/P * d_h elements: 128 B .. 1 KiB for the
+// supported d_h and dtypes, always a whole number of 128-byte lines. The
+// kernel therefore copies 16-byte words straight from HBM to HBM: a wave's
+// 64 lanes read 1 KiB of consecutive source words and write them as runs of
+// at least 128 contiguous bytes, so every line read and written is a full
+// line. Staging through LDS would add a round trip without making any access
+// wider. Values are never converted; bits are copied as they are.
+#include "common.h"
+#include "kernels.h"
+
+namespace ulysses {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // 16-byte words per thread in flight
+
+struct PermArgs {
+  const u32x4* __restrict__ src;
+  u32x4* __restrict__ dst;
+  uint32_t total;            // 16-byte words in the tensor
+  FastDiv fU, f3, f2, f1;    // source extents: [n0][n1][n2][n3][U]
+  uint32_t s0, s1, s2, s3;   // destination strides (words) of source coords i0..i3
+};
+
+__global__ __launch_bounds__(kThreads) void perm_kernel(PermArgs a) {
+  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+  u32x4 val[kUnroll];
+  uint32_t dsto[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t idx = base + u * kThreads;
+    if (idx < a.total) val[u] = __builtin_nontemporal_load(a.src + idx);
+    const uint32_t run = fdiv(idx, a.fU);
+    const uint32_t w = idx - run * a.fU.d;
+    const uint32_t t3 = fdiv(run, a.f3);
+    const uint32_t i3 = run - t3 * a.f3.d;
+    const uint32_t t2 = fdiv(t3, a.f2);
+    const uint32_t i2 = t3 - t2 * a.f2.d;
+    const uint32_t i0 = fdiv(t2, a.f1);
+    const uint32_t i1 = t2 - i0 * a.f1.d;
+    dsto[u] = i0 * a.s0 + i1 * a.s1 + i2 * a.s2 + i3 * a.s3 + w;
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t idx = base + u * kThreads;
+    if (idx < a.total) __builtin_nontemporal_store(val[u], a.dst + dsto[u]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, bool seq_to_head,
+                                hipStream_t stream) {
+  const uint32_t U = s.run_bytes / 16;  // words per (token, head-group) slab
+  const uint32_t P = s.P, B = s.B, Lp = s.Lp;
+  PermArgs a;
+  a.src = static_cast<const u32x4*>(src);
+  a.dst = static_cast<u32x4*>(dst);
+  a.total = s.total_words;
+  a.fU = make_fastdiv(U);
+  if (seq_to_head) {
+    // source [r][b][t][p][w]  ->  destination [p][b][r][t][w]
+    a.f1 = make_fastdiv(B);
+    a.f2 = make_fastdiv(Lp);
+    a.f3 = make_fastdiv(P);
+    a.s0 = Lp * U;             // r
+    a.s1 = P * Lp * U;         // b
+    a.s2 = U;                  // t
+    a.s3 = B * P * Lp * U;     // p
+  } else {
+    // source [p][b][r][t][w]  ->  destination [r][b][t][p][w]
+    a.f1 = make_fastdiv(B);
+    a.f2 = make_fastdiv(P);
+    a.f3 = make_fastdiv(Lp);
+    a.s0 = U;                  // p
+    a.s1 = Lp * P * U;         // b
+    a.s2 = B * Lp * P * U;     // r
+    a.s3 = P * U;              // t
+  }
+  const uint32_t per_block = kThreads * kUnroll;
+  const uint32_t blocks = (a.total + per_block - 1) / per_block;
+  hipLaunchKernelGGL(perm_kernel, dim3(blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ulysses

@@ -1,0 +1,141 @@
+/*
+ * ulysses.h -- C ABI of the Ulysses per-rank hot path on one AMD Instinct
+ * MI355X (gfx950): the sequence<->head layout change over P virtual ranks and
+ * exact full-sequence attention (forward and backward) on one rank's heads.
+ *
+ * Sources of the operations (web pages on DeepSpeed-Ulysses, arXiv 2309.14509):
+ *  - "Ulysses Sequence Parallelism: A Temporary Change of Layout" (pinyu.ai):
+ *    sections "Use the other independent axis" and "One attention block, end
+ *    to end" give the layout change [B, L/P, H, d_h] -> [B, L, H/P, d_h] and
+ *    back, and section "Head-count constraints" the rule H % P == 0.
+ *  - paper-graph summary of arXiv 2309.14509, section 3.4.1: contiguous token
+ *    chunks before the change, contiguous head groups after it; section 3.2
+ *    item 3 and 3.4.5: per-head scaled dot-product attention, causal or not,
+ *    on the full sequence with no communication.
+ *  - papers.chlience.com reading note, section 5.1: O'_p = softmax(Q'_p K'_p^T /
+ *    sqrt(d_h)) V'_p on rank p's head group.
+ *
+ * Conventions shared by every entry point
+ *  - Element types: ULYSSES_BF16 (bfloat16) or ULYSSES_FP32. The layout
+ *    changes move raw bits and accept either. bf16 attention accumulates in
+ *    fp32 and rounds its outputs to nearest-even bf16.
+ *  - Dense row-major layouts, all pointers are device pointers:
+ *      seq buffer  [P][B][L/P][H][d_h]   (rank-major token shards; for B = 1
+ *                                         byte-identical to a global [1][L][H][d_h])
+ *      head buffer [P][B][L][H/P][d_h]   (rank p holds heads p*H/P .. (p+1)*H/P-1)
+ *      attention operands: ONE rank's head block [B][L][H/P][d_h]; pass B*P as B
+ *      with the whole head buffer to run every rank's head group at once.
+ *      lse         [B][H/P][L] float32, natural-log log-sum-exp of each query
+ *                  row's scaled scores.
+ *  - Causal: key j is visible to query i iff j <= i, on global token positions.
+ *    Scale: exactly 1/sqrt(d_h).
+ *  - Ownership: the caller allocates and owns every buffer, the workspace
+ *    included. The library never allocates, frees or synchronises; all work is
+ *    enqueued on `stream` (a hipStream_t passed as void*, NULL = null stream)
+ *    in stream order, so outputs are ready when the stream reaches that point.
+ *    Inputs are read only. Outputs must not overlap inputs or each other.
+ *  - Errors: every function returns a ulysses_status. Arguments are validated
+ *    before any HIP call, so a rejected call touches no device state. After
+ *    validation a launch failure reported by the runtime returns
+ *    ULYSSES_HIP_ERROR; faults inside a kernel surface at the caller's next
+ *    synchronisation, as usual for asynchronous work.
+ *  - Limits: d_h in {64, 128}; the bf16 attention kernels need L % 128 == 0 is
+ *    NOT required (ragged tails are masked); each tensor below 2^32 16-byte
+ *    words (64 GiB).
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ulysses_status {
+  ULYSSES_OK = 0,
+  ULYSSES_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad flag */
+  ULYSSES_NOT_DIVISIBLE = 2,      /* H % P != 0 or L % P != 0 */
+  ULYSSES_UNSUPPORTED = 3,        /* d_h or dtype or size outside what the kernels implement */
+  ULYSSES_MISALIGNED = 4,         /* a pointer not 16-byte aligned */
+  ULYSSES_ALIASING = 5,           /* an output overlaps an input or another output */
+  ULYSSES_WORKSPACE_TOO_SMALL = 6,
+  ULYSSES_HIP_ERROR = 7           /* the HIP runtime rejected a launch */
+} ulysses_status;
+
+typedef enum ulysses_dtype {
+  ULYSSES_BF16 = 0,
+  ULYSSES_FP32 = 1
+} ulysses_dtype;
+
+/*
+ * First all-to-all of one attention block, as an on-device permutation over P
+ * virtual ranks: x_seq [P][B][L/P][H][d_h] -> x_head [P][B][L][H/P][d_h], with
+ *   x_head[p][b][r*L/P + t][j][:] = x_seq[r][b][t][p*H/P + j][:].
+ * Every sender r cuts its local heads into P groups; receiver p concatenates
+ * the token blocks it gets, in sender order (pinyu.ai, "Use the other
+ * independent axis"; paper-graph summary, section 3.4.1). Bits are copied
+ * unchanged (NaN payloads included). Not in place: x_head must not overlap x_seq.
+ */
+int ulysses_seq_to_head(const void* x_seq, void* x_head,
+                        int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P,
+                        int dtype, void* stream);
+
+/*
+ * Second all-to-all, the inverse permutation: x_head [P][B][L][H/P][d_h] ->
+ * x_seq [P][B][L/P][H][d_h], with
+ *   x_seq[r][b][t][p*H/P + j][:] = x_head[p][b][r*L/P + t][j][:]
+ * (pinyu.ai, "One attention block, end to end", step 4; paper-graph summary,
+ * section 3.4.1, "After attention: the reverse transformation").
+ */
+int ulysses_head_to_seq(const void* x_head, void* x_seq,
+                        int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P,
+                        int dtype, void* stream);
+
+/*
+ * Exact attention on one rank's head group (papers.chlience.com note,
+ * section 5.1; paper-graph summary, sections 3.2 and 3.4.5):
+ *   O = softmax(Q K^T / sqrt(d_h)) V  per (batch, local head), full length L,
+ * causal (causal = 1) or bidirectional (causal = 0). q, k, v, o are
+ * [B][L][H/P][d_h] of `dtype`; lse [B][H/P][L] float32 receives
+ * m_i + ln(sum_j exp(S_ij - m_i)) over the visible keys of row i, which the
+ * backward pass uses to recompute the probabilities.
+ */
+int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P,
+                     int causal, int dtype, void* stream);
+
+/*
+ * Gradient of the attention above w.r.t. q, k, v given dO = d_o (the pages
+ * train with the method but leave its backward implicit; this is the exact
+ * gradient). With P_ij = exp(S_ij - lse_i) recomputed from the saved lse:
+ *   D_i = sum_e dO_ie O_ie, dV = P^T dO, dS = P o (dO V^T - D),
+ *   dQ = dS K / sqrt(d_h), dK = dS^T Q / sqrt(d_h).
+ * All tensors [B][L][H/P][d_h] of `dtype` except lse (as written by
+ * ulysses_attn_fwd for the same q, k, v). `workspace` is device scratch of at
+ * least ulysses_attn_bwd_workspace_bytes(...) bytes, 256-byte aligned,
+ * owned by the caller; its contents on entry do not matter.
+ */
+int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* d_o, const float* lse,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P,
+                     int causal, int dtype, void* stream);
+
+/* Workspace ulysses_attn_bwd needs for these sizes (0 if the sizes are invalid). */
+size_t ulysses_attn_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t d_h,
+                                        int64_t P, int causal, int dtype);
+
+/* Static, NUL-terminated name of a status code ("ULYSSES_OK", ...). */
+const char* ulysses_status_string(int status);
+
+/* Text of the last HIP error this thread saw inside the library, or "". */
+const char* ulysses_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H */

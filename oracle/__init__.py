@@ -7,6 +7,6 @@ with the HIP library.
 from .ulysses_oracle import *  # noqa: F401,F403
 from .ulysses_oracle import (attn_bwd, attn_bwd_head, attn_dkv_cols, attn_fwd,  # noqa: F401
                              attn_fwd_head, attn_rows, bf16_bits_to_f64, check_divisible,
-                             error_stats, head_to_seq, head_to_seq_source_rows,
+                             error_stats, head_to_seq, head_to_seq_part, head_to_seq_source_rows,
                              monolithic_attention_fwd, seq_to_head, seq_to_head_part,
                              seq_to_head_source_rows, to_f64, ulysses_attention_fwd)

@@ -141,6 +141,12 @@ def seq_to_head_part(x: np.ndarray, B: int, L: int, H: int, d: int, P: int, p: i
     return _move_rows(x, rows, d, (B, L, H // P, d))
 
 
+def head_to_seq_part(y: np.ndarray, B: int, L: int, H: int, d: int, P: int, r: int) -> np.ndarray:
+    """Token-rank r's block [B, L/P, H, d] of head_to_seq, for bounded host memory."""
+    rows = head_to_seq_source_rows(B, L, H, P).reshape(P, -1)[r]
+    return _move_rows(y, rows, d, (B, L // P, H, d))
+
+
 # ---------------------------------------------------------------------------
 # exact attention, forward (definition written out, fp64, two-pass softmax)
 # ---------------------------------------------------------------------------

@@ -70,6 +70,10 @@ def test_round_trips_and_bijection(B, L, H, d, P):
     assert np.array_equal(np.sort(rows), np.arange(B * L * H))  # every source row used exactly once
     rows2 = oracle.head_to_seq_source_rows(B, L, H, P)
     assert np.array_equal(rows2[rows], np.arange(B * L * H))   # the two maps are inverse
+    for p in range(P):  # per-rank blocks agree with the whole tensors
+        np.testing.assert_array_equal(oracle.seq_to_head_part(x, B, L, H, d, P, p), y[p])
+        np.testing.assert_array_equal(oracle.head_to_seq_part(z, B, L, H, d, P, p),
+                                      oracle.head_to_seq(z, B, L, H, d, P)[p])
 
 
 def test_one_rank_is_identity():
