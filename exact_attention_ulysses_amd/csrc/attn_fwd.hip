@@ -37,13 +37,17 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int L, int Hh, int nqb, int nhb, float sl2) {
-  constexpr int BM = 128, BN = 64, ST = D + 8, KS = D / 16, DT = D / 32;
+  constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CH = BN * CPR / 256;         // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * ST];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[BN * ST];
+  constexpr int RSTEP = 256 / CPR;           // rows between a thread's chunks
+  constexpr int KST = Stride<D>::row;        // K is read along rows (S^T = K Q^T)
+  constexpr int VST = Stride<D>::col;        // V is read transposed (O^T += V^T P^T)
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KST];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VST];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / nhb;  // longest rows first
   const int hb = bid % nhb;            // (batch, head) pair
@@ -54,7 +58,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const __bf16* kh = k + head_off;
   const __bf16* vh = v + head_off;
   const int q0 = qb * BM;
-  const int qrow = q0 + 32 * wave + l32;
+  const int qw0 = q0 + 32 * wave;      // first query row of this wave
+  const int qrow = qw0 + l32;
 
   // Q^T as the B operand: lane holds Q[qrow][16 ks + 8 hl .. +7]
   bf16x8 qf[KS];
@@ -69,91 +74,112 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  // running maximum in log2 units and this lane's share of the running sum
   float m_run = -INFINITY, l_run = 0.f;
 
   const int kend = CAUSAL ? min(L, q0 + BM) : L;
   const int nkb = (kend + BN - 1) / BN;
 
+  // staging: thread tid moves chunks of rows srow + j * RSTEP, columns scol .. scol+7
+  const int srow = tid / CPR, scol = (tid % CPR) * 8;
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int kb) {
+    const int r0 = kb * BN + srow;
+    const __bf16* kt = kh + (size_t)r0 * rs + scol;
+    const __bf16* vt = vh + (size_t)r0 * rs + scol;
+    if (kb * BN + BN <= L) {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        kreg[j] = *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs);
+        vreg[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool in = r0 + j * RSTEP < L;
+        kreg[j] = in ? *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
+        vreg[j] = in ? *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int key = kb * BN + row;
-      if (key < L) {
-        kreg[j] = *reinterpret_cast<const u32x4*>(kh + (size_t)key * rs + col);
-        vreg[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)key * rs + col);
-      } else {
-        kreg[j] = u32x4{0, 0, 0, 0};
-        vreg[j] = u32x4{0, 0, 0, 0};
-      }
+      *reinterpret_cast<u32x4*>(&Ks[buf][(srow + j * RSTEP) * KST + scol]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&Vs[buf][(srow + j * RSTEP) * VST + scol]) = vreg[j];
     }
   };
 
   load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (nkb > 1) load_tile(1);
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * ST + col) = kreg[j];
-      *reinterpret_cast<u32x4*>(Vs + row * ST + col) = vreg[j];
-    }
-    __syncthreads();
-    if (kb + 1 < nkb) load_tile(kb + 1);
+    const int cur = kb & 1;
+    const __bf16* Kc = Ks[cur];
+    const __bf16* Vc = Vs[cur];
     const int k0 = kb * BN;
 
-    // S^T = K Q^T: two 32-key sub-tiles
-    f32x16 s[2];
+    // S^T = K Q^T for the tile's two 32-key halves (independent MFMA chains)
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      s[mt] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[mt] = mfma32(frag_row<ST>(Ks, 32 * mt, 16 * ks, lane), qf[ks], s[mt]);
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma32(frag_row<KST>(Kc, 0, 16 * ks, lane), qf[ks], s0);
+      s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
     }
 
-    const bool need_mask = CAUSAL ? (k0 + BN - 1 > q0 + 32 * wave) : (k0 + BN > L);
+    // only tiles that cross the diagonal (or the end of the sequence) need a mask
+    const bool edge = CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > L);
+    if (edge) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (CAUSAL ? (key > qrow) : (key >= L)) s0[e] = -INFINITY;
+        if (CAUSAL ? (key + 32 > qrow) : (key + 32 >= L)) s1[e] = -INFINITY;
+      }
+    }
+
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[mt][e] * sl2;
-        if (need_mask) {
-          const int key = k0 + 32 * mt + 8 * (e >> 2) + 4 * hl + (e & 3);
-          if (CAUSAL ? (key > qrow) : (key >= L)) x = -INFINITY;
-        }
-        s[mt][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    const float mcand = mx * sl2;
+    // The running maximum is raised only when some row's maximum grew by more
+    // than 8 (log2 units): in between, probabilities stay below 2^8 and the
+    // O accumulators need no rescaling. Normalisation at the end is exact.
+    if (__ballot(mcand > m_run + 8.f)) {
+      const float m2 = fmaxf(m_run, mcand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_run = m2;
+    }
+    const float nm = -m_run;
     float rsum = 0.f;
+    bf16x8 pf[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[mt][e] - m_new);
-        s[mt][e] = p;
+      for (int i = 0; i < 8; ++i) {
+        const float x = (c < 2) ? s0[8 * (c & 1) + i] : s1[8 * (c & 1) + i];
+        const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, nm));
         rsum += p;
+        pf[c][i] = (__bf16)p;
       }
     }
-    l_run = l_run * alpha + rsum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    l_run += rsum;
 
     // O^T += V^T P^T over four 16-key chunks
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const bf16x8 pf = acc_chunk_bf16(s[c >> 1], c & 1);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<ST>(Vs, 16 * c, 32 * dt, lane), pf, oacc[dt]);
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<VST>(Vc, 16 * c, 32 * dt, lane), pf[c], oacc[dt]);
     }
+
+    if (kb + 1 < nkb) store_tile(cur ^ 1);
+    if (kb + 2 < nkb) load_tile(kb + 2);
+    __syncthreads();
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -166,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
     }
-    if (hl == 0) lse[(size_t)hb * L + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (hl == 0) lse[(size_t)hb * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 

@@ -16,6 +16,16 @@
 
 namespace ulysses {
 
+// LDS row strides (elements) by how a tile is read; gfx950 LDS has 64 banks of
+// 4 bytes, serves 16-byte reads in passes of 16 lanes and the transposing
+// 8-byte reads in passes of 32 lanes (measured). A stride of 4 banks mod 64
+// keeps 16 consecutive rows apart for row reads; 16 banks mod 64 keeps the 4
+// rows of a transposing read apart; 12 banks mod 64 is conflict-free for row
+// reads and 2-way for transposing reads (tiles read both ways).
+template <int D> struct Stride;
+template <> struct Stride<128> { static constexpr int row = 136, col = 160, both = 152; };
+template <> struct Stride<64> { static constexpr int row = 72, col = 96, both = 88; };
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 

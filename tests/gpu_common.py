@@ -36,25 +36,30 @@ def to_f64(t_or_bits, dtype: str) -> np.ndarray:
     return oracle.to_f64(bits, dtype)
 
 
-def round_f64_to_bf16(x: np.ndarray) -> np.ndarray:
-    """Exact values rounded to the nearest bf16 (ties to even), kept as float64.
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits): 2^(e-8) for |x| in [2^(e-1), 2^e)."""
+    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
+    return np.ldexp(1.0, e - 8)
 
-    A bf16 output cannot be closer to the exact value than this; for |x| >= 4
-    the spacing of bf16 (2^-5) alone exceeds an absolute error of 1e-2.
+
+def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True):
+    """Compare a kernel output with the fp64 oracle value `want`.
+
+    bf16 outputs: every element within max(1e-2, one bf16 ulp of the exact
+    value) -- the two differ only for |x| >= 2, where bf16 spacing alone
+    (2^-6 and up) exceeds 1e-2 -- and ||got - want||_F / ||want||_F <= 5e-3.
+    fp32 outputs: max |got - want| <= 1e-5. With fro=False only the
+    elementwise bar applies (for hand-picked rows, whose norm says nothing
+    about the whole tensor's relative Frobenius error).
     """
-    m, e = np.frexp(np.asarray(x, dtype=np.float64))
-    return np.ldexp(np.rint(m * 256.0), e - 8)
-
-
-def check_close(name, got, want, dtype, max_abs=None, rel_fro=None):
-    """bf16: max |got - bf16(want)| <= 1e-2 and ||got - want||_F / ||want||_F <= 5e-3;
-    fp32: max |got - want| <= 1e-5. `want` is the fp64 oracle value."""
     st = oracle.error_stats(got, want)
     if dtype == "bf16":
         ma = BF16_MAX_ABS if max_abs is None else max_abs
         rf = BF16_REL_FRO if rel_fro is None else rel_fro
-        st["max_abs_vs_rounded"] = oracle.error_stats(got, round_f64_to_bf16(want))["max_abs"]
-        ok = st["max_abs_vs_rounded"] <= ma and st["rel_fro"] <= rf
+        err = np.abs(np.asarray(got, dtype=np.float64) - want)
+        allowed = np.maximum(ma, bf16_ulp(want))
+        st["max_err_over_allowed"] = float(np.max(err / allowed)) if err.size else 0.0
+        ok = st["max_err_over_allowed"] <= 1.0 and (st["rel_fro"] <= rf or not fro)
     else:
         ma = FP32_MAX_ABS if max_abs is None else max_abs
         ok = st["max_abs"] <= ma
