@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=12288,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=49152,
                     help="prefix length of one head that the fp64 oracle runs fwd+bwd on")
     return ap.parse_args()
 

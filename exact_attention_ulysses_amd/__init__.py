@@ -16,7 +16,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libulysses.so")
+# The in-tree build; ULYSSES_LIB_PATH may name another build of the same library
+# (kernel variants compared side by side).
+LIB_PATH = os.environ.get("ULYSSES_LIB_PATH") or os.path.join(_HERE, "libulysses.so")
 
 BF16 = 0
 FP32 = 1

@@ -22,6 +22,8 @@
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_frag.h"
@@ -61,13 +63,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, int Hh, int nhb, float sl2, float scale) {
-  constexpr int BQ = 64, ST = D + 8, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256;
-  __shared__ __attribute__((aligned(16))) __bf16 Qs[BQ * ST];
-  __shared__ __attribute__((aligned(16))) __bf16 Ds[BQ * ST];   // dO tile
-  __shared__ __attribute__((aligned(16))) float lse2s[BQ];
-  __shared__ __attribute__((aligned(16))) float dls[BQ];
+  constexpr int BQ = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256, RSTEP = 256 / CPR;
+  constexpr int ST = Stride<D>::both;  // Q and dO tiles are read along rows and transposed
+  __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
+  __shared__ __attribute__((aligned(16))) __bf16 Ds[2][BQ * ST];   // dO tiles
+  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float dls[2][BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = blockIdx.x / nhb;  // key block 0 has the most query tiles under the causal mask
   const int hb = blockIdx.x % nhb;
   const int b = hb / Hh, h = hb - b * Hh;
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const __bf16* doh = d_o + head_off;
   const float* lseh = lse + (size_t)hb * L;
   const float* dlh = delta + (size_t)hb * L;
-  const int k0w = kb * 128 + 32 * wave;
+  const int k0w = kb * 128 + 32 * wave;   // first key of this wave
   const int key = k0w + l32;
 
   // K and V rows of this lane's key as B operands (k = head dim)
@@ -101,82 +105,120 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
   const int qstart = CAUSAL ? kb * 128 : 0;
   const int nqt = (L - qstart + BQ - 1) / BQ;
+  const int srow = tid / CPR, scol = (tid % CPR) * 8;
   u32x4 qreg[CH], dreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
   auto load_tile = [&](int qt) {
-    const int q0 = qstart + qt * BQ;
+    const int r0 = qstart + qt * BQ + srow;
+    const __bf16* qt_ = qh + (size_t)r0 * rs + scol;
+    const __bf16* dt_ = doh + (size_t)r0 * rs + scol;
+    if (qstart + qt * BQ + BQ <= L) {
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int qi = q0 + row;
-      if (qi < L) {
-        qreg[j] = *reinterpret_cast<const u32x4*>(qh + (size_t)qi * rs + col);
-        dreg[j] = *reinterpret_cast<const u32x4*>(doh + (size_t)qi * rs + col);
-      } else {
-        qreg[j] = u32x4{0, 0, 0, 0};
-        dreg[j] = u32x4{0, 0, 0, 0};
+      for (int j = 0; j < CH; ++j) {
+        qreg[j] = *reinterpret_cast<const u32x4*>(qt_ + (size_t)(j * RSTEP) * rs);
+        dreg[j] = *reinterpret_cast<const u32x4*>(dt_ + (size_t)(j * RSTEP) * rs);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool in = r0 + j * RSTEP < L;
+        qreg[j] = in ? *reinterpret_cast<const u32x4*>(qt_ + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
+        dreg[j] = in ? *reinterpret_cast<const u32x4*>(dt_ + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
       }
     }
     if (tid < BQ) {
-      const int qi = q0 + tid;
+      const int qi = qstart + qt * BQ + tid;
       // rows past the end get lse = +inf, so their probabilities are exactly 0
       lse_r = qi < L ? lseh[qi] * kLog2e : INFINITY;
       dl_r = qi < L ? dlh[qi] : 0.f;
     }
   };
-
-  load_tile(0);
-  for (int qt = 0; qt < nqt; ++qt) {
-    const int q0 = qstart + qt * BQ;
-    __syncthreads();
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(Qs + row * ST + col) = qreg[j];
-      *reinterpret_cast<u32x4*>(Ds + row * ST + col) = dreg[j];
+      *reinterpret_cast<u32x4*>(&Qs[buf][(srow + j * RSTEP) * ST + scol]) = qreg[j];
+      *reinterpret_cast<u32x4*>(&Ds[buf][(srow + j * RSTEP) * ST + scol]) = dreg[j];
     }
     if (tid < BQ) {
-      lse2s[tid] = lse_r;
-      dls[tid] = dl_r;
+      lse2s[buf][tid] = lse_r;
+      dls[buf][tid] = dl_r;
     }
-    __syncthreads();
-    if (qt + 1 < nqt) load_tile(qt + 1);
+  };
 
+  // One query tile: S = Q K^T and dP = dO V^T for two 32-row halves, the
+  // probabilities and dS of each half, then dV^T += dO^T P and dK^T += Q^T dS.
+  auto tile = [&](int qt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int cur = qt & 1;
+    const int q0 = qstart + qt * BQ;
+    const __bf16* Qc = Qs[cur];
+    const __bf16* Dc = Ds[cur];
+    f32x16 s[2], dp[2];
+    auto scores = [&](int u) {
+      s[u] = f32x16{};
+      dp[u] = f32x16{};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = mfma32(frag_row<ST>(Qs, 32 * u, 16 * ks, lane), kf[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dp = mfma32(frag_row<ST>(Ds, 32 * u, 16 * ks, lane), vf[ks], dp);
-      const bool need_mask = CAUSAL && (k0w + 31 > q0 + 32 * u);
+      for (int ks = 0; ks < KS; ++ks) {
+        s[u] = mfma32(frag_row<ST>(Qc, 32 * u, 16 * ks, lane), kf[ks], s[u]);
+        dp[u] = mfma32(frag_row<ST>(Dc, 32 * u, 16 * ks, lane), vf[ks], dp[u]);
+      }
+    };
+    auto grads = [&](int u) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int r0 = 32 * u + 8 * a + 4 * hl;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2s + r0);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dls + r0);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[cur][r0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[cur][r0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * a + i;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -l4[i]));
-          if (need_mask && key > q0 + r0 + i) p = 0.f;
-          s[e] = p;
-          dp[e] = p * (dp[e] - d4[i]);
+          float p = __builtin_amdgcn_exp2f(fmaf(s[u][e], sl2, -l4[i]));
+          float ds = p * (dp[u][e] - d4[i]);
+          if (MASK && key > q0 + r0 + i) {  // keys above the query row
+            p = 0.f;
+            ds = 0.f;
+          }
+          s[u][e] = p;
+          dp[u][e] = ds;
         }
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pf = acc_chunk_bf16(s, c);
-        const bf16x8 dsf = acc_chunk_bf16(dp, c);
+        const bf16x8 pf = acc_chunk_bf16(s[u], c);
+        const bf16x8 dsf = acc_chunk_bf16(dp[u], c);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          dvacc[dt] = mfma32(frag_col<ST>(Ds, 32 * u + 16 * c, 32 * dt, lane), pf, dvacc[dt]);
-          dkacc[dt] = mfma32(frag_col<ST>(Qs, 32 * u + 16 * c, 32 * dt, lane), dsf, dkacc[dt]);
+          dvacc[dt] = mfma32(frag_col<ST>(Dc, 32 * u + 16 * c, 32 * dt, lane), pf, dvacc[dt]);
+          dkacc[dt] = mfma32(frag_col<ST>(Qc, 32 * u + 16 * c, 32 * dt, lane), dsf, dkacc[dt]);
         }
       }
-    }
+    };
+    // both halves' S/dP first: one half's MFMAs can overlap the other's vector work
+    scores(0);
+    scores(1);
+    grads(0);
+    grads(1);
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (nqt > 1) load_tile(1);
+  // under the causal mask only the first two query tiles reach above a key of this block
+  const int nmask = CAUSAL ? min(nqt, 2) : 0;
+  auto advance = [&](int qt) {
+    if (qt + 1 < nqt) store_tile((qt & 1) ^ 1);
+    if (qt + 2 < nqt) load_tile(qt + 2);
+    __syncthreads();
+  };
+  int qt = 0;
+  for (; qt < nmask; ++qt) {
+    tile(qt, std::integral_constant<bool, true>{});
+    advance(qt);
+  }
+  for (; qt < nqt; ++qt) {
+    tile(qt, std::integral_constant<bool, false>{});
+    advance(qt);
   }
 
   if (key < L) {
@@ -198,11 +240,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dq, int L, int Hh, int nqb, int nhb, float sl2, float scale) {
-  constexpr int BM = 128, BN = 64, ST = D + 8, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256;
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[BN * ST];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[BN * ST];
+  constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256, RSTEP = 256 / CPR;
+  constexpr int KST = Stride<D>::both;  // K: rows for S^T = K Q^T, transposed for dQ^T += K^T dS^T
+  constexpr int VST = Stride<D>::row;   // V: rows for dP^T = V dO^T
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KST];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VST];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = nqb - 1 - (int)blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;
   const int b = hb / Hh, h = hb - b * Hh;
@@ -211,7 +256,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const __bf16* kh = k + head_off;
   const __bf16* vh = v + head_off;
   const int q0 = qb * BM;
-  const int qrow = q0 + 32 * wave + l32;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + l32;
   const bool valid = qrow < L;
 
   bf16x8 qf[KS], df[KS];
@@ -225,7 +271,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       df[ks] = bf16x8{};
     }
   }
-  const float lse2 = valid ? lse[(size_t)hb * L + qrow] * kLog2e : 0.f;
+  const float nlse2 = valid ? -lse[(size_t)hb * L + qrow] * kLog2e : 0.f;
   const float dl = valid ? delta[(size_t)hb * L + qrow] : 0.f;
 
   f32x16 dqacc[DT];
@@ -234,63 +280,84 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 
   const int kend = CAUSAL ? min(L, q0 + BM) : L;
   const int nkb = (kend + BN - 1) / BN;
+  const int srow = tid / CPR, scol = (tid % CPR) * 8;
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int kb) {
+    const int r0 = kb * BN + srow;
+    const __bf16* kt = kh + (size_t)r0 * rs + scol;
+    const __bf16* vt = vh + (size_t)r0 * rs + scol;
+    if (kb * BN + BN <= L) {
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      const int kk = kb * BN + row;
-      if (kk < L) {
-        kreg[j] = *reinterpret_cast<const u32x4*>(kh + (size_t)kk * rs + col);
-        vreg[j] = *reinterpret_cast<const u32x4*>(vh + (size_t)kk * rs + col);
-      } else {
-        kreg[j] = u32x4{0, 0, 0, 0};
-        vreg[j] = u32x4{0, 0, 0, 0};
+      for (int j = 0; j < CH; ++j) {
+        kreg[j] = *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs);
+        vreg[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const bool in = r0 + j * RSTEP < L;
+        kreg[j] = in ? *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
+        vreg[j] = in ? *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
       }
     }
   };
-
-  load_tile(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c / CPR, col = (c % CPR) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * ST + col) = kreg[j];
-      *reinterpret_cast<u32x4*>(Vs + row * ST + col) = vreg[j];
+      *reinterpret_cast<u32x4*>(&Ks[buf][(srow + j * RSTEP) * KST + scol]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&Vs[buf][(srow + j * RSTEP) * VST + scol]) = vreg[j];
     }
-    __syncthreads();
-    if (kb + 1 < nkb) load_tile(kb + 1);
-    const int k0 = kb * BN;
-    const bool need_mask = CAUSAL ? (k0 + BN - 1 > q0 + 32 * wave) : (k0 + BN > L);
+  };
 
+  auto tile = [&](int kb, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const int cur = kb & 1;
+    const __bf16* Kc = Ks[cur];
+    const __bf16* Vc = Vs[cur];
+    const int k0 = kb * BN;
+    const bool edge = EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > L));
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = mfma32(frag_row<ST>(Ks, 32 * mt, 16 * ks, lane), qf[ks], s);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dp = mfma32(frag_row<ST>(Vs, 32 * mt, 16 * ks, lane), df[ks], dp);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32(frag_row<KST>(Kc, 32 * mt, 16 * ks, lane), qf[ks], s);
+        dp = mfma32(frag_row<VST>(Vc, 32 * mt, 16 * ks, lane), df[ks], dp);
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, -lse2));
-        if (need_mask) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[e], sl2, nlse2));
+        s[e] = p * (dp[e] - dl);  // dS^T of this 32-key half
+      }
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
           const int kk = k0 + 32 * mt + 8 * (e >> 2) + 4 * hl + (e & 3);
-          if (CAUSAL ? (kk > qrow) : (kk >= L)) p = 0.f;
+          if (CAUSAL ? (kk > qrow) : (kk >= L)) s[e] = 0.f;
         }
-        s[e] = p * (dp[e] - dl);  // dS^T of this 32-key sub-tile
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const bf16x8 dsf = acc_chunk_bf16(s, c);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          dqacc[dt] = mfma32(frag_col<ST>(Ks, 32 * mt + 16 * c, 32 * dt, lane), dsf, dqacc[dt]);
+          dqacc[dt] = mfma32(frag_col<KST>(Kc, 32 * mt + 16 * c, 32 * dt, lane), dsf, dqacc[dt]);
       }
     }
-  }
+    if (kb + 1 < nkb) store_tile(cur ^ 1);
+    if (kb + 2 < nkb) load_tile(kb + 2);
+    __syncthreads();
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (nkb > 1) load_tile(1);
+  // as in the forward pass: only the last two key tiles (causal) or a ragged last tile need a mask
+  const int nsteady = CAUSAL ? max(0, nkb - 2) : (L % BN ? nkb - 1 : nkb);
+  int kb = 0;
+  for (; kb < nsteady; ++kb) tile(kb, std::integral_constant<bool, false>{});
+  for (; kb < nkb; ++kb) tile(kb, std::integral_constant<bool, true>{});
 
   if (valid) {
     __bf16* row = dq + head_off + (size_t)qrow * rs;

@@ -22,6 +22,8 @@
 //   the small fp32 workloads; precision reference for the tests).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma_frag.h"
@@ -110,11 +112,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  if (nkb > 1) load_tile(1);
-  for (int kb = 0; kb < nkb; ++kb) {
+  // One key tile. EDGE tiles cross the diagonal (or the end of the sequence)
+  // and need the mask; the steady-state loop runs without it.
+  auto tile = [&](int kb, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int cur = kb & 1;
     const __bf16* Kc = Ks[cur];
     const __bf16* Vc = Vs[cur];
@@ -128,9 +129,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
     }
 
-    // only tiles that cross the diagonal (or the end of the sequence) need a mask
-    const bool edge = CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > L);
-    if (edge) {
+    if (EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > L))) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
@@ -180,7 +179,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     if (kb + 1 < nkb) store_tile(cur ^ 1);
     if (kb + 2 < nkb) load_tile(kb + 2);
     __syncthreads();
-  }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (nkb > 1) load_tile(1);
+  // causal: only the last two key tiles reach above a query row of this block;
+  // otherwise only a ragged last tile holds keys past the end
+  const int nsteady = CAUSAL ? max(0, nkb - 2) : (L % BN ? nkb - 1 : nkb);
+  int kb = 0;
+  for (; kb < nsteady; ++kb) tile(kb, std::integral_constant<bool, false>{});
+  for (; kb < nkb; ++kb) tile(kb, std::integral_constant<bool, true>{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
