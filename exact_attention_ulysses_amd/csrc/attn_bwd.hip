@@ -58,8 +58,19 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
   }
 }
 
+// dK/dV as producer/consumer wave pairs. A workgroup owns 128 keys and has 8
+// waves: producer wave w (0..3) and consumer wave w+4 share keys 32w..32w+31
+// and, with the usual in-order placement of a workgroup's waves on the four
+// SIMDs, one SIMD. For each 64-row query tile the producer forms S = Q K^T and
+// dP = dO V^T (K and V of its keys stay in its registers), the probabilities
+// P and dS = P o (dP - delta), and writes both as bf16 MFMA operands to LDS;
+// one tile later its consumer reads them and accumulates dV^T += dO^T P and
+// dK^T += Q^T dS. Neither role needs more than 256 registers, so the pair
+// shares a SIMD and the producer's exponentials and products run while the
+// consumer's MFMAs do. Tiles are double buffered; each step ends with two
+// barriers (hand-over, then the staging of the next tile).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, int Hh, int nhb, float sl2, float scale) {
@@ -69,10 +80,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 Ds[2][BQ * ST];   // dO tiles
   __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
   __shared__ __attribute__((aligned(16))) float dls[2][BQ];
+  // hand-over: [buffer][producer][P or dS][half u * 2 + chunk c][lane]
+  __shared__ __attribute__((aligned(16))) bf16x8 hand[2][4][2][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kb = blockIdx.x / nhb;  // key block 0 has the most query tiles under the causal mask
+  const bool producer = wave < 4;
+  const int pw = wave & 3;                 // key group of this wave (shared by the pair)
+  const int kb = blockIdx.x / nhb;         // key block 0 has the most query tiles under the causal mask
   const int hb = blockIdx.x % nhb;
   const int b = hb / Hh, h = hb - b * Hh;
   const size_t rs = (size_t)Hh * D;
@@ -81,30 +96,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const __bf16* doh = d_o + head_off;
   const float* lseh = lse + (size_t)hb * L;
   const float* dlh = delta + (size_t)hb * L;
-  const int k0w = kb * 128 + 32 * wave;   // first key of this wave
-  const int key = k0w + l32;
-
-  // K and V rows of this lane's key as B operands (k = head dim)
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (key < L) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(k + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(v + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
-    } else {
-      kf[ks] = bf16x8{};
-      vf[ks] = bf16x8{};
-    }
-  }
-  f32x16 dkacc[DT], dvacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dkacc[dt] = f32x16{};
-    dvacc[dt] = f32x16{};
-  }
+  const int key = kb * 128 + 32 * pw + l32;
 
   const int qstart = CAUSAL ? kb * 128 : 0;
   const int nqt = (L - qstart + BQ - 1) / BQ;
+  // under the causal mask only the first two query tiles reach above a key of this block
+  const int nmask = CAUSAL ? min(nqt, 2) : 0;
+
+  // staging of Q, dO, lse, delta by the producer waves (threads 0..255)
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
   u32x4 qreg[CH], dreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
@@ -145,91 +144,115 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
 
-  // One query tile: S = Q K^T and dP = dO V^T for two 32-row halves, the
-  // probabilities and dS of each half, then dV^T += dO^T P and dK^T += Q^T dS.
-  auto tile = [&](int qt, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = qt & 1;
-    const int q0 = qstart + qt * BQ;
-    const __bf16* Qc = Qs[cur];
-    const __bf16* Dc = Ds[cur];
-    f32x16 s[2], dp[2];
-    auto scores = [&](int u) {
-      s[u] = f32x16{};
-      dp[u] = f32x16{};
+  if (producer) {
+    // ---------------- producer: S, dP, P, dS ----------------
+    bf16x8 kf[KS], vf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s[u] = mfma32(frag_row<ST>(Qc, 32 * u, 16 * ks, lane), kf[ks], s[u]);
-        dp[u] = mfma32(frag_row<ST>(Dc, 32 * u, 16 * ks, lane), vf[ks], dp[u]);
+    for (int ks = 0; ks < KS; ++ks) {
+      if (key < L) {
+        kf[ks] = *reinterpret_cast<const bf16x8*>(k + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
+        vf[ks] = *reinterpret_cast<const bf16x8*>(v + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
+      } else {
+        kf[ks] = bf16x8{};
+        vf[ks] = bf16x8{};
       }
-    };
-    auto grads = [&](int u) {
+    }
+    auto produce = [&](int qt, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int cur = qt & 1;
+      const int q0 = qstart + qt * BQ;
+      const __bf16* Qc = Qs[cur];
+      const __bf16* Dc = Ds[cur];
+      f32x16 sc[2], dp[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r0 = 32 * u + 8 * a + 4 * hl;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[cur][r0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[cur][r0]);
+      for (int u = 0; u < 2; ++u) {
+        sc[u] = f32x16{};
+        dp[u] = f32x16{};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * a + i;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[u][e], sl2, -l4[i]));
-          float ds = p * (dp[u][e] - d4[i]);
-          if (MASK && key > q0 + r0 + i) {  // keys above the query row
-            p = 0.f;
-            ds = 0.f;
+        for (int ks = 0; ks < KS; ++ks) {
+          sc[u] = mfma32(frag_row<ST>(Qc, 32 * u, 16 * ks, lane), kf[ks], sc[u]);
+          dp[u] = mfma32(frag_row<ST>(Dc, 32 * u, 16 * ks, lane), vf[ks], dp[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int r0 = 32 * u + 8 * a + 4 * hl;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[cur][r0]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[cur][r0]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * a + i;
+            float p = __builtin_amdgcn_exp2f(fmaf(sc[u][e], sl2, -l4[i]));
+            float ds = p * (dp[u][e] - d4[i]);
+            if (MASK && key > q0 + r0 + i) {  // keys above the query row
+              p = 0.f;
+              ds = 0.f;
+            }
+            sc[u][e] = p;
+            dp[u][e] = ds;
           }
-          s[u][e] = p;
-          dp[u][e] = ds;
         }
-      }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 pf = acc_chunk_bf16(s[u], c);
-        const bf16x8 dsf = acc_chunk_bf16(dp[u], c);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dvacc[dt] = mfma32(frag_col<ST>(Dc, 32 * u + 16 * c, 32 * dt, lane), pf, dvacc[dt]);
-          dkacc[dt] = mfma32(frag_col<ST>(Qc, 32 * u + 16 * c, 32 * dt, lane), dsf, dkacc[dt]);
+        for (int c = 0; c < 2; ++c) {
+          hand[cur][pw][0][2 * u + c][lane] = acc_chunk_bf16(sc[u], c);
+          hand[cur][pw][1][2 * u + c][lane] = acc_chunk_bf16(dp[u], c);
         }
       }
     };
-    // both halves' S/dP first: one half's MFMAs can overlap the other's vector work
-    scores(0);
-    scores(1);
-    grads(0);
-    grads(1);
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  if (nqt > 1) load_tile(1);
-  // under the causal mask only the first two query tiles reach above a key of this block
-  const int nmask = CAUSAL ? min(nqt, 2) : 0;
-  auto advance = [&](int qt) {
-    if (qt + 1 < nqt) store_tile((qt & 1) ^ 1);
-    if (qt + 2 < nqt) load_tile(qt + 2);
+    load_tile(0);
+    store_tile(0);
     __syncthreads();
-  };
-  int qt = 0;
-  for (; qt < nmask; ++qt) {
-    tile(qt, std::integral_constant<bool, true>{});
-    advance(qt);
-  }
-  for (; qt < nqt; ++qt) {
-    tile(qt, std::integral_constant<bool, false>{});
-    advance(qt);
-  }
-
-  if (key < L) {
-    __bf16* dkrow = dk + head_off + (size_t)key * rs;
-    __bf16* dvrow = dv + head_off + (size_t)key * rs;
+    if (nqt > 1) load_tile(1);
+    for (int s = 0; s <= nqt; ++s) {
+      if (s < nmask)
+        produce(s, std::integral_constant<bool, true>{});
+      else if (s < nqt)
+        produce(s, std::integral_constant<bool, false>{});
+      __syncthreads();  // hand-over of tile s; consumers are done with tile s-1's buffers
+      if (s + 1 < nqt) store_tile((s + 1) & 1);
+      if (s + 2 < nqt) load_tile(s + 2);
+      __syncthreads();  // tile s+1 staged
+    }
+  } else {
+    // ---------------- consumer: dV, dK ----------------
+    f32x16 dkacc[DT], dvacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      dkacc[dt] = f32x16{};
+      dvacc[dt] = f32x16{};
+    }
+    __syncthreads();  // tile 0 staged
+    for (int s = 0; s <= nqt; ++s) {
+      if (s >= 1) {
+        const int prev = (s - 1) & 1;
+        const __bf16* Qc = Qs[prev];
+        const __bf16* Dc = Ds[prev];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        *reinterpret_cast<bf16x4*>(dkrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dkacc[dt], a, scale);
-        *reinterpret_cast<bf16x4*>(dvrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dvacc[dt], a, 1.f);
+        for (int uc = 0; uc < 4; ++uc) {
+          const bf16x8 pf = hand[prev][pw][0][uc][lane];
+          const bf16x8 dsf = hand[prev][pw][1][uc][lane];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            dvacc[dt] = mfma32(frag_col<ST>(Dc, 16 * uc, 32 * dt, lane), pf, dvacc[dt]);
+            dkacc[dt] = mfma32(frag_col<ST>(Qc, 16 * uc, 32 * dt, lane), dsf, dkacc[dt]);
+          }
+        }
+      }
+      __syncthreads();
+      __syncthreads();
+    }
+    if (key < L) {
+      __bf16* dkrow = dk + head_off + (size_t)key * rs;
+      __bf16* dvrow = dv + head_off + (size_t)key * rs;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          *reinterpret_cast<bf16x4*>(dkrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dkacc[dt], a, scale);
+          *reinterpret_cast<bf16x4*>(dvrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dvacc[dt], a, 1.f);
+        }
       }
     }
   }
@@ -511,7 +534,7 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
   const float scale = 1.f / sqrtf((float)D);
   const float sl2 = scale * kLog2e;
   const int nkb = (s.L + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)nkb * nhb), dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)nkb * nhb), dim3(512), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                      (__bf16*)dk, (__bf16*)dv, s.L, s.Hh, nhb, sl2, scale);
   e = hipGetLastError();
