@@ -22,8 +22,11 @@ LIB = os.path.join(PKG, "libulysses.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops
+# -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
+# -fno-honor-nans: no kernel produces or tests for NaN (masking uses -inf), so
+# max/min need no NaN canonicalisation of MFMA results.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+          "-fno-honor-nans",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include")]
 

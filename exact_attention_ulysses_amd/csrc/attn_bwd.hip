@@ -103,27 +103,23 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   // under the causal mask only the first two query tiles reach above a key of this block
   const int nmask = CAUSAL ? min(nqt, 2) : 0;
 
-  // staging of Q, dO, lse, delta by the producer waves (threads 0..255)
+  // staging of Q, dO, lse, delta by the producer waves (threads 0..255) through
+  // buffer loads; rows past the end of the sequence read as zero
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
+  const uint32_t head_bytes = (uint32_t)((size_t)L * rs * 2);
+  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(qh, head_bytes);
+  const __amdgpu_buffer_rsrc_t drs = head_rsrc(doh, head_bytes);
+  uint32_t voff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rs + scol) * 2);
   u32x4 qreg[CH], dreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
   auto load_tile = [&](int qt) {
-    const int r0 = qstart + qt * BQ + srow;
-    const __bf16* qt_ = qh + (size_t)r0 * rs + scol;
-    const __bf16* dt_ = doh + (size_t)r0 * rs + scol;
-    if (qstart + qt * BQ + BQ <= L) {
+    const uint32_t soff = (uint32_t)(qstart + qt * BQ) * (uint32_t)(rs * 2);
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        qreg[j] = *reinterpret_cast<const u32x4*>(qt_ + (size_t)(j * RSTEP) * rs);
-        dreg[j] = *reinterpret_cast<const u32x4*>(dt_ + (size_t)(j * RSTEP) * rs);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const bool in = r0 + j * RSTEP < L;
-        qreg[j] = in ? *reinterpret_cast<const u32x4*>(qt_ + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
-        dreg[j] = in ? *reinterpret_cast<const u32x4*>(dt_ + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
-      }
+    for (int j = 0; j < CH; ++j) {
+      qreg[j] = buf_load16(qrs, voff[j] + soff, 0);
+      dreg[j] = buf_load16(drs, voff[j] + soff, 0);
     }
     if (tid < BQ) {
       const int qi = qstart + qt * BQ + tid;
@@ -304,24 +300,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int kend = CAUSAL ? min(L, q0 + BM) : L;
   const int nkb = (kend + BN - 1) / BN;
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
+  const uint32_t head_bytes = (uint32_t)((size_t)L * rs * 2);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vh, head_bytes);
+  uint32_t voff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rs + scol) * 2);
+  const uint32_t tile_bytes = (uint32_t)(BN * rs * 2);
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int kb) {
-    const int r0 = kb * BN + srow;
-    const __bf16* kt = kh + (size_t)r0 * rs + scol;
-    const __bf16* vt = vh + (size_t)r0 * rs + scol;
-    if (kb * BN + BN <= L) {
+    const uint32_t soff = (uint32_t)kb * tile_bytes;
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        kreg[j] = *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs);
-        vreg[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const bool in = r0 + j * RSTEP < L;
-        kreg[j] = in ? *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
-        vreg[j] = in ? *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
-      }
+    for (int j = 0; j < CH; ++j) {
+      kreg[j] = buf_load16(krs, voff[j] + soff, 0);
+      vreg[j] = buf_load16(vrs, voff[j] + soff, 0);
     }
   };
   auto store_tile = [&](int buf) {

@@ -82,26 +82,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int kend = CAUSAL ? min(L, q0 + BM) : L;
   const int nkb = (kend + BN - 1) / BN;
 
-  // staging: thread tid moves chunks of rows srow + j * RSTEP, columns scol .. scol+7
+  // staging: thread tid moves chunks of rows srow + j * RSTEP, columns scol .. scol+7,
+  // through buffer loads (constant per-lane offset, scalar tile offset)
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
+  const uint32_t head_bytes = (uint32_t)((size_t)L * rs * 2);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vh, head_bytes);
+  uint32_t voff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rs + scol) * 2);
+  const uint32_t tile_bytes = (uint32_t)(BN * rs * 2);
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int kb) {
-    const int r0 = kb * BN + srow;
-    const __bf16* kt = kh + (size_t)r0 * rs + scol;
-    const __bf16* vt = vh + (size_t)r0 * rs + scol;
-    if (kb * BN + BN <= L) {
+    const uint32_t soff = (uint32_t)kb * tile_bytes;
 #pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        kreg[j] = *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs);
-        vreg[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < CH; ++j) {
-        const bool in = r0 + j * RSTEP < L;
-        kreg[j] = in ? *reinterpret_cast<const u32x4*>(kt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
-        vreg[j] = in ? *reinterpret_cast<const u32x4*>(vt + (size_t)(j * RSTEP) * rs) : u32x4{0, 0, 0, 0};
-      }
+    for (int j = 0; j < CH; ++j) {
+      kreg[j] = buf_load16(krs, voff[j] + soff, 0);
+      vreg[j] = buf_load16(vrs, voff[j] + soff, 0);
     }
   };
   auto store_tile = [&](int buf) {

@@ -29,6 +29,21 @@ template <> struct Stride<64> { static constexpr int row = 72, col = 96, both = 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// Buffer resource over one head's rows [base, base + bytes): loads whose
+// vector offset lies past the range return zero (hardware range check), so
+// tiles that run past the end of the sequence need no guards. Callers put the
+// whole offset in the vector operand (scalar offset 0) so that the checked
+// offset is the full one. Word 3 = 0x00020000 is the raw 32-bit data format of
+// gfx9-family buffer descriptors.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -76,6 +76,8 @@ int attn_dims(int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P, int causa
   if (causal != 0 && causal != 1) return ULYSSES_INVALID_ARGUMENT;
   const int64_t Hh = H / P;
   if (B * Hh > (int64_t(1) << 24) || B * L * Hh >= (int64_t(1) << 31)) return ULYSSES_UNSUPPORTED;
+  // the kernels address one head's rows (plus a padded last tile) with 32-bit byte offsets
+  if ((L + 256) * Hh * d_h * elem_size(dtype) >= (int64_t(1) << 32)) return ULYSSES_UNSUPPORTED;
   s->B = (int)B;
   s->L = (int)L;
   s->Hh = (int)Hh;

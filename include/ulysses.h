@@ -39,9 +39,10 @@
  *    validation a launch failure reported by the runtime returns
  *    ULYSSES_HIP_ERROR; faults inside a kernel surface at the caller's next
  *    synchronisation, as usual for asynchronous work.
- *  - Limits: d_h in {64, 128}; the bf16 attention kernels need L % 128 == 0 is
- *    NOT required (ragged tails are masked); each tensor below 2^32 16-byte
- *    words (64 GiB).
+ *  - Limits: d_h in {64, 128}; any L >= 1 (partial tiles are masked); each
+ *    tensor below 32 GiB; for attention, one head's rows (L * H/P * d_h
+ *    elements, plus 256 rows of slack) below 4 GiB, and B * L * H/P < 2^31.
+ *    Calls outside these limits return ULYSSES_UNSUPPORTED.
  */
 #ifndef ULYSSES_H
 #define ULYSSES_H

@@ -86,6 +86,8 @@ def test_forward_validation():
     assert fwd(o=A + 1024) == 5                      # output overlaps q
     assert fwd(lse=A + 3 * GB + 64) == 5             # lse overlaps o
     assert fwd(lse=A + 2 * GB) == 5                  # lse overlaps v
+    # one head's rows span 4 GiB: past the kernels' 32-bit row offsets
+    assert fwd(L=1 << 20, H=16, P=1, q=A, k=A + 8 * GB, v=A + 16 * GB, o=A + 24 * GB, lse=A + 32 * GB) == 3
 
 
 def bwd(ws_bytes=None, B=1, L=1024, H=8, d=128, P=4, causal=1, dtype=U.BF16, **ptrs):
