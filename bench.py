@@ -11,10 +11,19 @@ the whole step time (transposes included); per-op figures come from HIP
 events recorded on the launch stream around every call in the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+HBM traffic of the dominant op (roofline "traffic"): two rocprofv3 counter
+runs of this script with --calibration-copy, one collecting FETCH_SIZE and
+one WRITE_SIZE, are reduced with --summarize-traffic into
+profiles/hbm_traffic_<workload>.json; the counters are scaled by what they
+read for a device copy of known size. The summary carries a hash of the
+kernel sources and is used only while the sources still match it.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +39,78 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+CALIB_BYTES = 1 << 30   # device copy of known size for counter calibration
+
+
+def kernel_sources_hash() -> str:
+    """sha256 over the HIP sources and build script (the counters belong to one build)."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "exact_attention_ulysses_amd")
+    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+
+
+OP_KERNELS = {"attn_fwd": ("attn_fwd_bf16_kernel",),
+              "attn_bwd": ("bwd_delta_kernel", "bwd_dkdv_bf16_kernel", "bwd_dq_bf16_kernel"),
+              "perm": ("perm_kernel",)}
+
+
+def summarize_traffic(workload: str, fetch_dir: str, write_dir: str, cmd_fetch: str, cmd_write: str) -> None:
+    """Reduce two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) to per-op bytes."""
+    import csv
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_f = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs]
+    copy_w = [v for k, vs in write.items() if "copyBuffer" in k for v in vs]
+    if not copy_f or not copy_w:
+        raise SystemExit("no calibration copy found in the counter runs (use --calibration-copy)")
+    fscale, wscale = CALIB_BYTES / max(copy_f), CALIB_BYTES / max(copy_w)
+
+    def avg(vals, names):
+        out = 0.0
+        for n in names:
+            hits = [sum(v) / len(v) for k, v in vals.items() if n in k]
+            out += hits[0] if hits else 0.0
+        return out
+
+    ops = {op: {"read_bytes": avg(fetch, ks) * fscale, "write_bytes": avg(write, ks) * wscale}
+           for op, ks in OP_KERNELS.items()}
+    res = {"workload": workload, "kernel_sources_sha256": kernel_sources_hash(),
+           "fetch_scale": fscale, "write_scale": wscale, "per_launch": ops,
+           "commands": [cmd_fetch, cmd_write]}
+    with open(traffic_path(workload), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def load_traffic(workload: str, op: str):
+    """HBM bytes per launch of `op` from the committed summary, or None if absent or stale."""
+    try:
+        with open(traffic_path(workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256") != kernel_sources_hash():
+        return None
+    b = t["per_launch"][op]
+    return b["read_bytes"] + b["write_bytes"]
+
+
 def npairs(L: int, causal: bool) -> int:
     return L * (L + 1) // 2 if causal else L * L
 
@@ -43,6 +124,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=49152,
                     help="prefix length of one head that the fp64 oracle runs fwd+bwd on")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 runs)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
+                    help="reduce two rocprofv3 counter runs to profiles/hbm_traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -81,6 +166,10 @@ def cpu_baseline(wl, seq_host, tokens: int):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        from workloads import HEADLINE
+        summarize_traffic(args.workload or HEADLINE, *args.summarize_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU exchange is not "
               "part of this build", file=sys.stderr)
@@ -172,7 +261,7 @@ def main():
     roofline = {"bound": "mfma", "kernel": ("ulysses_attn_bwd (delta, dK/dV and dQ launches)" if dom == "attn_bwd"
                                             else "ulysses_attn_fwd"),
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": load_traffic(wl.key, dom),
                 "per_launch": {"flops": dom_flops, "ms": avg[dom]}}
 
     detail = {
@@ -188,6 +277,13 @@ def main():
     if wl.backward:
         detail.update({"attn_bwd_ms": avg["attn_bwd"],
                        "attn_bwd_TFLOPs": bwd_flops / (avg["attn_bwd"] * 1e-3) / 1e12})
+
+    if args.calibration_copy:
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
