@@ -5,7 +5,8 @@ cpu_baseline leg of bench.py, never by the product path. It shares no code
 with the HIP library.
 """
 from .ulysses_oracle import *  # noqa: F401,F403
-from .ulysses_oracle import (attn_bwd, attn_bwd_head, attn_dkv_cols, attn_fwd,  # noqa: F401
+from .ulysses_oracle import (attn_bwd, attn_bwd_gqa, attn_bwd_head, attn_fwd_gqa, check_gqa,
+                             head_to_seq_kv_grad, kv_replication, seq_to_head_kv, attn_dkv_cols, attn_fwd,  # noqa: F401
                              attn_fwd_head, attn_rows, bf16_bits_to_f64, check_divisible,
                              error_stats, head_to_seq, head_to_seq_part, head_to_seq_source_rows,
                              monolithic_attention_fwd, seq_to_head, seq_to_head_part,

@@ -31,6 +31,20 @@ What it computes (citations name a page and the passage on it):
       dV = P^T dO,  dP = dO V^T,  D_i = sum_e dO_ie O_ie,
       dS = P o (dP - D),  dQ = dS K / sqrt(d_h),  dK = dS^T Q / sqrt(d_h).
 
+* attn_fwd_gqa / attn_bwd_gqa -- grouped-query attention: H_q query heads share
+  H_kv < H_q key/value heads (pinyu.ai, section "Head-count constraints";
+  paper-graph summary, section 6.4). Query head h uses KV head h div (H_q/H_kv);
+  the gradient of a shared KV head is the sum over its query heads.
+  seq_to_head_kv / head_to_seq_kv_grad -- the K/V layout change: the ordinary
+  one when H_kv % P == 0, otherwise (P % H_kv == 0) every rank gathers the one
+  KV head its query heads use, so P/H_kv consecutive ranks hold a replica of it
+  (the replication the "Head-count constraints" section mentions); the
+  gradient map is the adjoint of that gather (replicas summed).
+
+* cross-attention -- attn_fwd_head / attn_bwd_head take keys of another length
+  than the queries (papers.chlience.com note, section 5.4 lists cross-attention
+  among the supported kinds); bidirectional only.
+
 Readings of points the pages leave open (kept in one place):
   * causal means key j is visible to query i iff j <= i (the diagonal is kept);
     positions are global token indices after the layout change;
@@ -151,8 +165,8 @@ def head_to_seq_part(y: np.ndarray, B: int, L: int, H: int, d: int, P: int, r: i
 # exact attention, forward (definition written out, fp64, two-pass softmax)
 # ---------------------------------------------------------------------------
 
-def _visible_keys(i1: int, L: int, causal: bool) -> int:
-    return i1 if causal else L
+def _visible_keys(i1: int, Lkv: int, causal: bool) -> int:
+    return min(i1, Lkv) if causal else Lkv
 
 
 def _scores(qb: np.ndarray, kk: np.ndarray, i0: int, causal: bool, scale: float) -> np.ndarray:
@@ -175,14 +189,21 @@ def _softmax_rows(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 
 def attn_fwd_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
                   row_block: int = ROW_BLOCK) -> Tuple[np.ndarray, np.ndarray]:
-    """One head: q, k, v [L, d] float64 -> O [L, d], LSE [L]."""
+    """One head: q [Lq, d], k, v [Lkv, d] float64 -> O [Lq, d], LSE [Lq].
+
+    Lq != Lkv is cross-attention (bidirectional only: the pages pair the
+    causal mask with self-attention).
+    """
     L, d = q.shape
+    Lkv = k.shape[0]
+    if causal and Lkv != L:
+        raise ValueError("causal attention needs Lq == Lkv")
     scale = 1.0 / math.sqrt(d)
     o = np.empty((L, d), dtype=np.float64)
     lse = np.empty((L,), dtype=np.float64)
     for i0 in range(0, L, row_block):
         i1 = min(L, i0 + row_block)
-        nk = _visible_keys(i1, L, causal)
+        nk = _visible_keys(i1, Lkv, causal)
         s = _scores(q[i0:i1], k[:nk], i0, causal, scale)
         p, lse[i0:i1] = _softmax_rows(s)
         o[i0:i1] = p @ v[:nk]
@@ -206,23 +227,27 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True,
 # ---------------------------------------------------------------------------
 
 def attn_bwd_head(q, k, v, do, causal: bool, row_block: int = ROW_BLOCK):
-    """One head: the exact gradient of <dO, O> w.r.t. q, k, v; all [L, d] float64.
+    """One head: the exact gradient of <dO, O> w.r.t. q, k, v (float64; q, do
+    [Lq, d], k, v [Lkv, d]).
 
     Per row block the probabilities are formed once and used for O, D, dP,
     dS and the three products; dK and dV accumulate over the row blocks.
     Returns (dq, dk, dv, o, lse, D).
     """
     L, d = q.shape
+    Lkv = k.shape[0]
+    if causal and Lkv != L:
+        raise ValueError("causal attention needs Lq == Lkv")
     scale = 1.0 / math.sqrt(d)
     dq = np.zeros((L, d))
-    dk = np.zeros((L, d))
-    dv = np.zeros((L, d))
+    dk = np.zeros((Lkv, d))
+    dv = np.zeros((Lkv, d))
     o = np.empty((L, d))
     lse = np.empty((L,))
     D = np.empty((L,))
     for i0 in range(0, L, row_block):
         i1 = min(L, i0 + row_block)
-        nk = _visible_keys(i1, L, causal)
+        nk = _visible_keys(i1, Lkv, causal)
         s = _scores(q[i0:i1], k[:nk], i0, causal, scale)
         p, lse[i0:i1] = _softmax_rows(s)
         ob = p @ v[:nk]
@@ -252,6 +277,88 @@ def attn_bwd(q, k, v, do, causal: bool = True, row_block: int = ROW_BLOCK):
             r = attn_bwd_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], causal, row_block)
             dq[b, :, h], dk[b, :, h], dv[b, :, h], o[b, :, h], lse[b, h], D[b, h] = r
     return dq, dk, dv, o, lse, D
+
+
+# ---------------------------------------------------------------------------
+# grouped-query attention: fewer K/V heads than query heads
+# (pinyu.ai, "Head-count constraints": GQA/MQA have fewer KV heads; a rank's
+# KV heads follow its query heads, replicated when P exceeds the KV heads)
+# ---------------------------------------------------------------------------
+
+def check_gqa(Hq: int, Hkv: int) -> int:
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"query heads {Hq} must be a multiple of KV heads {Hkv}")
+    return Hq // Hkv
+
+
+def attn_fwd_gqa(q, k, v, causal: bool = True, row_block: int = ROW_BLOCK):
+    """q [B, Lq, Hq, d], k, v [B, Lkv, Hkv, d]: query head h attends with KV head
+    h div (Hq/Hkv). Returns O [B, Lq, Hq, d], LSE [B, Hq, Lq]."""
+    B, Lq, Hq, d = q.shape
+    G = check_gqa(Hq, k.shape[2])
+    o = np.empty((B, Lq, Hq, d))
+    lse = np.empty((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            o[b, :, h], lse[b, h] = attn_fwd_head(q[b, :, h], k[b, :, h // G], v[b, :, h // G], causal, row_block)
+    return o, lse
+
+
+def attn_bwd_gqa(q, k, v, do, causal: bool = True, row_block: int = ROW_BLOCK):
+    """Gradient of attn_fwd_gqa: dQ per query head; dK, dV of a KV head are the
+    sums over the query heads that share it. Returns (dq, dk, dv)."""
+    B, Lq, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = check_gqa(Hq, Hkv)
+    dq = np.empty_like(q, dtype=np.float64)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            r = attn_bwd_head(q[b, :, h], k[b, :, h // G], v[b, :, h // G], do[b, :, h], causal, row_block)
+            dq[b, :, h] = r[0]
+            dk[b, :, h // G] += r[1]
+            dv[b, :, h // G] += r[2]
+    return dq, dk, dv
+
+
+def kv_replication(Hkv: int, P: int) -> int:
+    """Ranks per KV head group: 1 if the KV heads split evenly over P ranks,
+    P / Hkv if every rank needs one KV head replicated from a smaller set."""
+    if Hkv % P == 0:
+        return 1
+    if P % Hkv == 0:
+        return P // Hkv
+    raise ValueError(f"KV heads {Hkv} and P={P}: neither divides the other")
+
+
+def seq_to_head_kv(x: np.ndarray, B: int, L: int, Hkv: int, d: int, P: int) -> np.ndarray:
+    """K/V layout change. Hkv % P == 0: the ordinary seq_to_head over Hkv heads.
+    P % Hkv == 0: rank p receives KV head p div (P/Hkv) from every sender,
+    concatenated along the sequence -> [P, B, L, 1, d]."""
+    R = kv_replication(Hkv, P)
+    if R == 1:
+        return seq_to_head(x, B, L, Hkv, d, P)
+    out = np.empty((P, B, L, 1, d), dtype=x.dtype)
+    Lp = L // P
+    for p in range(P):
+        for r in range(P):
+            out[p, :, r * Lp:(r + 1) * Lp, 0] = x[r, :, :, p // R]
+    return out
+
+
+def head_to_seq_kv_grad(y: np.ndarray, B: int, L: int, Hkv: int, d: int, P: int) -> np.ndarray:
+    """Adjoint of seq_to_head_kv for dK/dV (float64): with replication the R
+    copies of a KV head are summed back into its token shards."""
+    R = kv_replication(Hkv, P)
+    if R == 1:
+        return head_to_seq(y, B, L, Hkv, d, P)
+    Lp = L // P
+    out = np.zeros((P, B, Lp, Hkv, d))
+    for p in range(P):
+        for r in range(P):
+            out[r, :, :, p // R] += y[p, :, r * Lp:(r + 1) * Lp, 0]
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -217,7 +217,7 @@ def _brute_force_attention(q, k, v, causal):
     L, d = len(q), len(q[0])
     out, lses = [], []
     for i in range(L):
-        js = range(i + 1) if causal else range(L)
+        js = range(i + 1) if causal else range(len(k))
         s = [sum(q[i][e] * k[j][e] for e in range(d)) / math.sqrt(d) for j in js]
         w = [math.exp(x) for x in s]
         z = sum(w)
@@ -400,3 +400,127 @@ def test_host_inputs_are_seeded_and_shaped():
         t = int(pos[0, h])
         row = np.abs(vals[t // 32, 0, t % 32, h]).mean()
         assert row > 4 * 0.5 * 0.5  # scaled by 8 from 0.5*N(0,1)
+
+
+# ---------------------------------------------------------------------------
+# grouped-query attention and cross-attention
+# ---------------------------------------------------------------------------
+
+def _bhld(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+
+
+@pytest.mark.parametrize("Hq,Hkv,causal", [(8, 2, True), (8, 1, False), (6, 3, True), (4, 4, False)])
+def test_gqa_matches_torch_sdpa_and_autograd_fp64(Hq, Hkv, causal):
+    # torch's enable_gqa shares KV head h // (Hq/Hkv) with query head h, the
+    # grouping of the pages' GQA/MQA (pinyu.ai, "Head-count constraints")
+    torch = pytest.importorskip("torch")
+    B, L, d = 2, 90, 16
+    q, do = _rand((B, L, Hq, d), 40), _rand((B, L, Hq, d), 41)
+    k, v = _rand((B, L, Hkv, d), 42), _rand((B, L, Hkv, d), 43)
+    o, lse = oracle.attn_fwd_gqa(q, k, v, causal, row_block=32)
+    dq, dk, dv = oracle.attn_bwd_gqa(q, k, v, do, causal, row_block=32)
+    tq, tk, tv = (_bhld(a).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, enable_gqa=True)
+    out.backward(_bhld(do))
+    back = lambda t: t.detach().numpy().transpose(0, 2, 1, 3)  # noqa: E731
+    np.testing.assert_allclose(o, back(out), rtol=0, atol=1e-12)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, back(ref), rtol=0, atol=1e-11)
+    # the textbook reduction: GQA is MHA on K/V heads repeated G times
+    G = Hq // Hkv
+    kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    om, lsem = oracle.attn_fwd(q, kr, vr, causal)
+    np.testing.assert_allclose(o, om, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lsem, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("Lq,Lkv", [(37, 100), (130, 21), (1, 64)])
+def test_cross_attention_matches_torch_fp64(Lq, Lkv):
+    # queries and keys of different lengths (cross-attention, papers.chlience.com
+    # note, section 5.4): bidirectional, every query sees every key
+    torch = pytest.importorskip("torch")
+    d = 24
+    q, do = _rand((Lq, d), 44), _rand((Lq, d), 45)
+    k, v = _rand((Lkv, d), 46), _rand((Lkv, d), 47)
+    o, lse = oracle.attn_fwd_head(q, k, v, False, row_block=16)
+    dq, dk, dv, o2, lse2, D = oracle.attn_bwd_head(q, k, v, do, False, row_block=16)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None])[0]
+    out.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, torch.logsumexp(tq @ tk.T / math.sqrt(d), -1).detach().numpy(),
+                               rtol=0, atol=1e-12)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=0, atol=1e-11)
+    bo, blse = _brute_force_attention(q[:5].tolist(), k.tolist(), v.tolist(), False)
+    np.testing.assert_allclose(o[:5], bo, rtol=1e-12, atol=1e-13)
+
+
+def test_cross_attention_rejects_causal_mask():
+    q, k = _rand((8, 4), 48), _rand((9, 4), 49)
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_head(q, k, k, True)
+    with pytest.raises(ValueError):
+        oracle.attn_bwd_head(q, k, k, q, True)
+
+
+def test_kv_replication_factor():
+    assert oracle.kv_replication(8, 8) == 1        # LLaMA-3-style 8 KV heads at P = 8
+    assert oracle.kv_replication(8, 4) == 1
+    assert oracle.kv_replication(2, 8) == 4
+    assert oracle.kv_replication(1, 4) == 4        # MQA: every rank holds the one KV head
+    for Hkv, P in ((3, 2), (4, 6)):
+        with pytest.raises(ValueError):
+            oracle.kv_replication(Hkv, P)
+    with pytest.raises(ValueError):
+        oracle.check_gqa(8, 3)
+
+
+@pytest.mark.parametrize("B,L,Hkv,d,P", [(2, 12, 1, 3, 4), (1, 16, 2, 2, 8), (2, 8, 4, 2, 2), (1, 6, 2, 1, 6)])
+def test_kv_layout_change_by_procedure_and_adjoint(B, L, Hkv, d, P):
+    rng = np.random.default_rng(50)
+    x = rng.integers(0, 2**16, size=(P, B, L // P, Hkv, d), dtype=np.uint16)
+    y = oracle.seq_to_head_kv(x, B, L, Hkv, d, P)
+    R = oracle.kv_replication(Hkv, P)
+    if R == 1:
+        np.testing.assert_array_equal(y, oracle.seq_to_head(x, B, L, Hkv, d, P))
+    else:
+        # every rank gathers one KV head over all tokens: the head shared by
+        # its query-head group, which R consecutive ranks hold alike
+        full = np.concatenate([x[r] for r in range(P)], axis=1)        # [B, L, Hkv, d]
+        assert y.shape == (P, B, L, 1, d)
+        for p in range(P):
+            np.testing.assert_array_equal(y[p, :, :, 0], full[:, :, p // R])
+    # the gradient map is the adjoint of the gather: <S x, g> == <x, S^T g>
+    xf = rng.standard_normal((P, B, L // P, Hkv, d))
+    g = rng.standard_normal(y.shape)
+    lhs = float(np.sum(oracle.seq_to_head_kv(xf, B, L, Hkv, d, P) * g))
+    rhs = float(np.sum(xf * oracle.head_to_seq_kv_grad(g, B, L, Hkv, d, P)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("Hq,Hkv,P", [(8, 2, 2), (8, 2, 4), (4, 1, 4), (8, 2, 8)])
+def test_gqa_pipeline_equals_monolithic(Hq, Hkv, P):
+    # each rank runs GQA on its query heads and the KV heads they share; the
+    # result and the gradients equal single-device GQA attention
+    B, L, d = 1, 32, 8
+    q, do = _rand((P, B, L // P, Hq, d), 51), _rand((P, B, L // P, Hq, d), 52)
+    k, v = _rand((P, B, L // P, Hkv, d), 53), _rand((P, B, L // P, Hkv, d), 54)
+    qh = oracle.seq_to_head(q, B, L, Hq, d, P)
+    doh = oracle.seq_to_head(do, B, L, Hq, d, P)
+    kh = oracle.seq_to_head_kv(k, B, L, Hkv, d, P)
+    vh = oracle.seq_to_head_kv(v, B, L, Hkv, d, P)
+    outs = [oracle.attn_fwd_gqa(qh[p], kh[p], vh[p], True)[0] for p in range(P)]
+    grads = [oracle.attn_bwd_gqa(qh[p], kh[p], vh[p], doh[p], True) for p in range(P)]
+    o = oracle.head_to_seq(np.stack(outs), B, L, Hq, d, P)
+    dq = oracle.head_to_seq(np.stack([g[0] for g in grads]), B, L, Hq, d, P)
+    dk = oracle.head_to_seq_kv_grad(np.stack([g[1] for g in grads]), B, L, Hkv, d, P)
+    dv = oracle.head_to_seq_kv_grad(np.stack([g[2] for g in grads]), B, L, Hkv, d, P)
+    glob = lambda a: np.concatenate(list(a), axis=1)  # noqa: E731  [P,B,L/P,..] -> [B,L,..]
+    om, _ = oracle.attn_fwd_gqa(glob(q), glob(k), glob(v), True)
+    dqm, dkm, dvm = oracle.attn_bwd_gqa(glob(q), glob(k), glob(v), glob(do), True)
+    for mine, ref in ((o, om), (dq, dqm), (dk, dkm), (dv, dvm)):
+        np.testing.assert_allclose(glob(mine), ref, rtol=0, atol=1e-13)
