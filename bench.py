@@ -3,9 +3,12 @@
 One step = the whole path over one batch of seeded synthetic input, inputs
 already resident in HBM:
     seq_to_head on Q, K, V (and dO)          -- full [P][B][L/P][H][d_h] tensors
+                                                (K, V: the K/V form, replicating
+                                                 K/V heads when P > H_kv)
     attention forward on rank 0's head group  -- [B][L][H/P][d_h], causal
     attention backward (workloads with a backward pass)
-    head_to_seq on O (and dQ, dK, dV)         -- full head buffers
+    head_to_seq on O (and dQ, dK, dV)         -- full head buffers (dK, dV: the
+                                                gradient form, summing replicas)
 Prints ONE JSON line. `value` is attention fwd(+bwd) algorithmic TFLOP/s over
 the whole step time (transposes included); per-op figures come from HIP
 events recorded on the launch stream around every call in the timed steps.
@@ -111,8 +114,9 @@ def load_traffic(workload: str, op: str):
     return b["read_bytes"] + b["write_bytes"]
 
 
-def npairs(L: int, causal: bool) -> int:
-    return L * (L + 1) // 2 if causal else L * L
+def npairs(L: int, causal: bool, Lk: int = 0) -> int:
+    """Visible (query, key) pairs of one head: causal self-attention or all L x Lk."""
+    return L * (L + 1) // 2 if causal else L * (Lk or L)
 
 
 def parse():
@@ -142,24 +146,31 @@ def cpu_baseline(wl, seq_host, tokens: int):
         threads = None
     cores = len(os.sched_getaffinity(0))
     B, L, H, d, P = wl.B, wl.L, wl.H, wl.d, wl.P
-    Ls = min(tokens, L)
+    Ls, Lks = min(tokens, L), min(tokens, wl.Lk)
     t0 = time.perf_counter()
-    heads = {n: oracle.seq_to_head_part(seq_host[n], B, L, H, d, P, 0) for n in seq_host}
+    heads, perm_bytes = {}, 0
+    for n, x in seq_host.items():
+        if n in ("k", "v"):
+            heads[n] = oracle.seq_to_head_kv(x, B, wl.Lk, wl.Hk, d, P)[0]
+            perm_bytes += x.nbytes // P + heads[n].nbytes     # rank 0's share of the reads, its block written
+        else:
+            heads[n] = oracle.seq_to_head_part(x, B, L, H, d, P, 0)
+            perm_bytes += 2 * x.nbytes // P
     t_perm = time.perf_counter() - t0
-    perm_bytes = 2 * sum(a.nbytes for a in seq_host.values()) // P   # one destination rank's share, read + write
-    f = {n: oracle.to_f64(heads[n][0, :Ls, 0], wl.dtype) for n in heads}
+    f = {n: oracle.to_f64(heads[n][0, :(Lks if n in ("k", "v") else Ls), 0], wl.dtype) for n in heads}
     t0 = time.perf_counter()
     if wl.backward:
         oracle.attn_bwd_head(f["q"], f["k"], f["v"], f["do"], wl.causal)
-        flops = 14 * d * npairs(Ls, wl.causal)
+        flops = 14 * d * npairs(Ls, wl.causal, Lks)
     else:
         oracle.attn_fwd_head(f["q"], f["k"], f["v"], wl.causal)
-        flops = 4 * d * npairs(Ls, wl.causal)
+        flops = 4 * d * npairs(Ls, wl.causal, Lks)
     t_attn = time.perf_counter() - t0
     return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": threads if threads else cores,
             "host_cores_visible": cores, "kind": "oracle",
             "sample": (f"fp64 numpy oracle, {'fwd+bwd' if wl.backward else 'fwd'} of head 0 of rank 0 over the "
-                       f"first {Ls} tokens of the same inputs ({t_attn:.1f} s); flops counted as on the GPU"),
+                       f"first {Ls} query and {Lks} key tokens of the same inputs ({t_attn:.1f} s); flops "
+                       f"counted as on the GPU"),
             "perm_GBps": perm_bytes / t_perm / 1e9,
             "perm_sample": f"seq_to_head of rank 0's share of {len(seq_host)} tensors ({t_perm:.1f} s)"}
 
@@ -181,6 +192,8 @@ def main():
 
     wl = WORKLOADS[args.workload or HEADLINE]
     B, L, H, d, P, Hh, causal = wl.B, wl.L, wl.H, wl.d, wl.P, wl.Hp, wl.causal
+    Lk, Hk = wl.Lk, wl.Hk
+    rep = P * wl.Hkp // Hk      # ranks holding each K/V head
     assert wl.dtype == "bf16", "bench.py measures the bf16 path"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -188,32 +201,43 @@ def main():
 
     ins = ["q", "k", "v"] + (["do"] if wl.backward else [])
     outs = ["o"] + (["dq", "dk", "dv"] if wl.backward else [])
+    kv = lambda n: n in ("k", "v", "dk", "dv")  # noqa: E731  (K/V-side tensors)
     seq = {n: device_tensor(wl, n, dev) for n in ins}
-    head = {n: torch.empty(wl.head_shape, dtype=torch.bfloat16, device=dev) for n in ins}
+    head = {n: torch.empty(wl.shape_of("fill_d" + n if kv(n) else "fill_o"), dtype=torch.bfloat16, device=dev)
+            for n in ins}
     # output head buffers: rank 0's block is written by attention, the other blocks hold seeded filler
     ohead = {n: device_tensor(wl, "fill_" + n, dev) for n in outs}
-    oseq = {n: torch.empty(wl.seq_shape, dtype=torch.bfloat16, device=dev) for n in outs}
+    oseq = {n: torch.empty(wl.shape_of(n[1:] if kv(n) else "q"), dtype=torch.bfloat16, device=dev) for n in outs}
     lse = torch.empty((B, Hh, L), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, U.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, causal)), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(max(1, U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, causal)),
+                     dtype=torch.uint8, device=dev)
     r0 = {n: head[n][0] for n in ins}
     o0 = {n: ohead[n][0] for n in outs}
     stream = torch.cuda.current_stream()
 
-    ops = []  # (name, callable)
+    ops = []  # (name, callable, HBM bytes read + written)
+    tq, tk = B * L * H * d * 2, B * Lk * Hk * d * 2     # seq-layout tensor bytes, query side and K/V side
     for n in ins:
-        ops.append(("seq_to_head", lambda n=n: U.ulysses_seq_to_head(seq[n], head[n], B, L, H, d, P)))
-    ops.append(("attn_fwd", lambda: U.ulysses_attn_fwd(r0["q"], r0["k"], r0["v"], o0["o"], lse, B, L, H, d, P,
-                                                       causal)))
+        if kv(n):
+            ops.append(("seq_to_head", lambda n=n: U.ulysses_seq_to_head_kv(seq[n], head[n], B, Lk, Hk, d, P),
+                        tk * (1 + rep)))
+        else:
+            ops.append(("seq_to_head", lambda n=n: U.ulysses_seq_to_head(seq[n], head[n], B, L, H, d, P), 2 * tq))
+    ops.append(("attn_fwd", lambda: U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], lse, B, L, Lk, H,
+                                                           Hk, d, P, causal), 0))
     if wl.backward:
-        ops.append(("attn_bwd", lambda: U.ulysses_attn_bwd(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], lse,
-                                                           o0["dq"], o0["dk"], o0["dv"], ws, B, L, H, d, P,
-                                                           causal)))
+        ops.append(("attn_bwd", lambda: U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], lse,
+                                                               o0["dq"], o0["dk"], o0["dv"], ws, B, L, Lk, H, Hk,
+                                                               d, P, causal), 0))
     for n in outs:
-        ops.append(("head_to_seq", lambda n=n: U.ulysses_head_to_seq(ohead[n], oseq[n], B, L, H, d, P)))
+        if kv(n):
+            ops.append(("head_to_seq", lambda n=n: U.ulysses_head_to_seq_kv_grad(ohead[n], oseq[n], B, Lk, Hk, d,
+                                                                                  P), tk * (1 + rep)))
+        else:
+            ops.append(("head_to_seq", lambda n=n: U.ulysses_head_to_seq(ohead[n], oseq[n], B, L, H, d, P), 2 * tq))
 
     def step(events=None):
-        for i, (_, fn) in enumerate(ops):
+        for i, (_, fn, _) in enumerate(ops):
             if events is not None:
                 events[i][0].record(stream)
             fn()
@@ -239,18 +263,16 @@ def main():
 
     per_op = {}
     for s in range(args.steps):
-        for i, (name, _) in enumerate(ops):
+        for i, (name, _, _) in enumerate(ops):
             per_op.setdefault(name, []).append(evs[s][i][0].elapsed_time(evs[s][i][1]))
     avg = {k: sum(v) / len(v) for k, v in per_op.items()}       # ms per launch of that op
-    calls = {k: len(v) // args.steps for k, v in per_op.items()}
 
-    npr = npairs(L, causal)
+    npr = npairs(L, causal, Lk)
     fwd_flops = 4 * d * npr * B * Hh
     bwd_flops = 10 * d * npr * B * Hh
     attn_flops = fwd_flops + (bwd_flops if wl.backward else 0)
-    tensor_bytes = B * L * H * d * 2
-    perm_ms = avg["seq_to_head"] * calls["seq_to_head"] + avg["head_to_seq"] * calls["head_to_seq"]
-    perm_bytes = 2 * tensor_bytes * (calls["seq_to_head"] + calls["head_to_seq"])
+    perm_ms = sum(v for k, vs in per_op.items() if k in ("seq_to_head", "head_to_seq") for v in vs) / args.steps
+    perm_bytes = sum(b for name, _, b in ops if name in ("seq_to_head", "head_to_seq"))
     attn_ms = avg["attn_fwd"] + (avg.get("attn_bwd", 0.0))
     value = attn_flops / (ms_step * 1e-3) / 1e12
 
@@ -290,12 +312,17 @@ def main():
         host = {n: seq[n].view(torch.int16).cpu().numpy().view("uint16") for n in ins}
         cpu = cpu_baseline(wl, host, args.cpu_sample_tokens)
 
+    metric = METRIC if wl.key == HEADLINE else METRIC.replace(
+        "causal attn", ("causal" if causal else "bidirectional") + (" grouped-query" if Hk != H else "")
+        + (" cross-" if Lk != L else " ") + "attn")
     line = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": metric, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, device-generated)",
         "config": {"workload": wl.key, "B": B, "L": L, "H": H, "d_h": d, "P": P, "local_heads": Hh,
-                   "causal": causal, "backward": wl.backward, "parallelism": "1 GPU, P virtual ranks"},
+                   "causal": causal, "backward": wl.backward, "parallelism": "1 GPU, P virtual ranks",
+                   **({"L_kv": Lk} if Lk != L else {}), **({"H_kv": Hk, "local_kv_heads": wl.Hkp}
+                                                          if Hk != H else {})},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
     }
     print(json.dumps(line), flush=True)

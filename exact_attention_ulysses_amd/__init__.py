@@ -28,8 +28,10 @@ STATUS_NAMES = {0: "ULYSSES_OK", 1: "ULYSSES_INVALID_ARGUMENT", 2: "ULYSSES_NOT_
                 3: "ULYSSES_UNSUPPORTED", 4: "ULYSSES_MISALIGNED", 5: "ULYSSES_ALIASING",
                 6: "ULYSSES_WORKSPACE_TOO_SMALL", 7: "ULYSSES_HIP_ERROR"}
 
-EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
-           "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_last_hip_error")
+EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad",
+           "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
+           "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa", "ulysses_attn_bwd_gqa_workspace_bytes",
+           "ulysses_status_string", "ulysses_last_hip_error")
 
 
 class UlyssesError(RuntimeError):
@@ -50,7 +52,8 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_ulysses_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     i64, vp, ci, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-    for name in ("ulysses_seq_to_head", "ulysses_head_to_seq"):
+    for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_kv",
+                 "ulysses_head_to_seq_kv_grad"):
         f = getattr(L, name)
         f.argtypes = [vp, vp, i64, i64, i64, i64, i64, ci, vp]
         f.restype = ci
@@ -60,6 +63,13 @@ def lib() -> ctypes.CDLL:
     L.ulysses_attn_bwd.restype = ci
     L.ulysses_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci, ci]
     L.ulysses_attn_bwd_workspace_bytes.restype = sz
+    L.ulysses_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.ulysses_attn_fwd_gqa.restype = ci
+    L.ulysses_attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.ulysses_attn_bwd_gqa.restype = ci
+    L.ulysses_attn_bwd_gqa_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, ci]
+    L.ulysses_attn_bwd_gqa_workspace_bytes.restype = sz
     L.ulysses_status_string.argtypes = [ci]
     L.ulysses_status_string.restype = ctypes.c_char_p
     L.ulysses_last_hip_error.argtypes = []
@@ -124,6 +134,79 @@ def ulysses_head_to_seq(x_head, x_seq, B: int, L: int, H: int, d_h: int, P: int,
     _check(st, "ulysses_head_to_seq")
 
 
+def kv_local_heads(H_kv: int, P: int) -> int:
+    """K/V heads per rank after ulysses_seq_to_head_kv (0 if H_kv and P are incompatible)."""
+    if H_kv % P == 0:
+        return H_kv // P
+    return 1 if P % H_kv == 0 else 0
+
+
+def _kv_sizes(where: str, B: int, L: int, H_kv: int, d_h: int, P: int):
+    hl = kv_local_heads(H_kv, P)
+    if hl == 0:
+        raise UlyssesError(2, where)
+    return B * L * H_kv * d_h, P * B * L * hl * d_h
+
+
+def ulysses_seq_to_head_kv(x_seq, x_head, B: int, L: int, H_kv: int, d_h: int, P: int, stream=None) -> None:
+    """K/V x_seq [P][B][L/P][H_kv][d_h] -> x_head [P][B][L][Hl][d_h] (K/V heads replicated when P > H_kv)."""
+    ns, nh = _kv_sizes("ulysses_seq_to_head_kv", B, L, H_kv, d_h, P)
+    st = lib().ulysses_seq_to_head_kv(_dev(x_seq, "x_seq", ns), _dev(x_head, "x_head", nh, x_seq.dtype),
+                                      B, L, H_kv, d_h, P, dtype_code(x_seq), _stream(stream))
+    _check(st, "ulysses_seq_to_head_kv")
+
+
+def ulysses_head_to_seq_kv_grad(dx_head, dx_seq, B: int, L: int, H_kv: int, d_h: int, P: int, stream=None) -> None:
+    """Gradient of ulysses_seq_to_head_kv: dx_head [P][B][L][Hl][d_h] -> dx_seq [P][B][L/P][H_kv][d_h]."""
+    ns, nh = _kv_sizes("ulysses_head_to_seq_kv_grad", B, L, H_kv, d_h, P)
+    st = lib().ulysses_head_to_seq_kv_grad(_dev(dx_head, "dx_head", nh), _dev(dx_seq, "dx_seq", ns, dx_head.dtype),
+                                           B, L, H_kv, d_h, P, dtype_code(dx_head), _stream(stream))
+    _check(st, "ulysses_head_to_seq_kv_grad")
+
+
+def _gqa_sizes(where: str, B: int, L_q: int, L_kv: int, H_q: int, H_kv: int, d_h: int, P: int):
+    hl = kv_local_heads(H_kv, P)
+    if H_q % P or H_q % H_kv or hl == 0:
+        raise UlyssesError(2, where)
+    return B * L_q * (H_q // P) * d_h, B * L_kv * hl * d_h, B * (H_q // P) * L_q
+
+
+def ulysses_attn_fwd_gqa(q, k, v, o, lse, B: int, L_q: int, L_kv: int, H_q: int, H_kv: int, d_h: int, P: int,
+                         causal: bool = True, stream=None) -> None:
+    """Attention with H_q query heads sharing H_kv K/V heads, queries and keys of lengths L_q, L_kv:
+    q, o [B][L_q][H_q/P][d_h]; k, v [B][L_kv][Hl][d_h]; lse [B][H_q/P][L_q] fp32."""
+    torch = _torch()
+    nq, nk, nl = _gqa_sizes("ulysses_attn_fwd_gqa", B, L_q, L_kv, H_q, H_kv, d_h, P)
+    st = lib().ulysses_attn_fwd_gqa(_dev(q, "q", nq), _dev(k, "k", nk, q.dtype), _dev(v, "v", nk, q.dtype),
+                                    _dev(o, "o", nq, q.dtype), _dev(lse, "lse", nl, torch.float32),
+                                    B, L_q, L_kv, H_q, H_kv, d_h, P, int(bool(causal)), dtype_code(q),
+                                    _stream(stream))
+    _check(st, "ulysses_attn_fwd_gqa")
+
+
+def ulysses_attn_bwd_gqa_workspace_bytes(B: int, L_q: int, L_kv: int, H_q: int, H_kv: int, d_h: int, P: int,
+                                         causal: bool = True, dtype: int = BF16) -> int:
+    return int(lib().ulysses_attn_bwd_gqa_workspace_bytes(B, L_q, L_kv, H_q, H_kv, d_h, P, int(bool(causal)),
+                                                          dtype))
+
+
+def ulysses_attn_bwd_gqa(q, k, v, o, d_o, lse, dq, dk, dv, workspace, B: int, L_q: int, L_kv: int, H_q: int,
+                         H_kv: int, d_h: int, P: int, causal: bool = True, stream=None) -> None:
+    """dQ, dK, dV of ulysses_attn_fwd_gqa (a shared K/V head gets the sum over its query heads)."""
+    torch = _torch()
+    nq, nk, nl = _gqa_sizes("ulysses_attn_bwd_gqa", B, L_q, L_kv, H_q, H_kv, d_h, P)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().ulysses_attn_bwd_gqa(
+        _dev(q, "q", nq), _dev(k, "k", nk, q.dtype), _dev(v, "v", nk, q.dtype), _dev(o, "o", nq, q.dtype),
+        _dev(d_o, "d_o", nq, q.dtype), _dev(lse, "lse", nl, torch.float32),
+        _dev(dq, "dq", nq, q.dtype), _dev(dk, "dk", nk, q.dtype), _dev(dv, "dv", nk, q.dtype),
+        workspace.data_ptr(), wbytes, B, L_q, L_kv, H_q, H_kv, d_h, P, int(bool(causal)), dtype_code(q),
+        _stream(stream))
+    _check(st, "ulysses_attn_bwd_gqa")
+
+
 def ulysses_attn_fwd(q, k, v, o, lse, B: int, L: int, H: int, d_h: int, P: int, causal: bool = True,
                      stream=None) -> None:
     """O = softmax(Q K^T / sqrt(d_h)) V on one rank's head block [B][L][H/P][d_h]; lse [B][H/P][L] fp32."""
@@ -163,5 +246,7 @@ def ulysses_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace, B: int, L: int
     _check(st, "ulysses_attn_bwd")
 
 
-__all__ = ["lib", "LIB_PATH", "BF16", "FP32", "UlyssesError", "EXPORTS", "ulysses_seq_to_head",
-           "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes"]
+__all__ = ["lib", "LIB_PATH", "BF16", "FP32", "UlyssesError", "EXPORTS", "kv_local_heads", "ulysses_seq_to_head",
+           "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad", "ulysses_attn_fwd",
+           "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa",
+           "ulysses_attn_bwd_gqa_workspace_bytes"]

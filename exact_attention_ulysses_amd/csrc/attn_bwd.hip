@@ -20,6 +20,11 @@
 //   dK^T += Q^T dS directly; dO^T and Q^T are read transposed from LDS.
 // bf16 dQ kernel: workgroup = 4 waves x 32 query rows; the forward kernel's
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
+// Grouped-query attention (pinyu.ai, section "Head-count constraints"): a key
+//   head shared by G query heads gets the sum of their gradients; the dK/dV
+//   workgroup walks the query tiles of all G heads in turn and accumulates
+//   into the same registers. Keys may be fewer or more than queries
+//   (cross-attention, bidirectional only).
 #include <math.h>
 
 #include <type_traits>
@@ -37,7 +42,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // delta[b][h][i] = sum_e dO[b][i][h][e] * O[b][i][h][e]; D/8 lanes per row.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o, const T* __restrict__ d_o,
-                                                        float* __restrict__ delta, int L, int Hh, int rows) {
+                                                        float* __restrict__ delta, int Lq, int Hq, int rows) {
   constexpr int G = D / 8;
   const int gt = blockIdx.x * 256 + threadIdx.x;
   const int r = gt / G, part = gt % G;
@@ -51,10 +56,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
 #pragma unroll
   for (int off = G / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (r < rows && part == 0) {
-    const int h = r % Hh;
-    const int bl = r / Hh;
-    const int b = bl / L, i = bl - b * L;
-    delta[((size_t)b * Hh + h) * L + i] = acc;
+    const int h = r % Hq;
+    const int bl = r / Hq;
+    const int b = bl / Lq, i = bl - b * Lq;
+    delta[((size_t)b * Hq + h) * Lq + i] = acc;
   }
 }
 
@@ -73,7 +78,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, int Hh, int nhb, float sl2, float scale) {
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
+    float scale) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256, RSTEP = 256 / CPR;
   constexpr int ST = Stride<D>::both;  // Q and dO tiles are read along rows and transposed
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
@@ -88,34 +94,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   const bool producer = wave < 4;
   const int pw = wave & 3;                 // key group of this wave (shared by the pair)
   const int kb = blockIdx.x / nhb;         // key block 0 has the most query tiles under the causal mask
-  const int hb = blockIdx.x % nhb;
-  const int b = hb / Hh, h = hb - b * Hh;
-  const size_t rs = (size_t)Hh * D;
-  const size_t head_off = ((size_t)b * L * Hh + h) * D;
-  const __bf16* qh = q + head_off;
-  const __bf16* doh = d_o + head_off;
-  const float* lseh = lse + (size_t)hb * L;
-  const float* dlh = delta + (size_t)hb * L;
+  const int hb = blockIdx.x % nhb;         // (batch, key head) pair
+  const int b = hb / Hk, hk = hb - b * Hk;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;   // row strides
+  // query heads hk*G .. hk*G + G-1 share this key head; g selects one of them
+  const size_t qoff = ((size_t)b * Lq * Hq + (size_t)hk * G) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + hk) * D;
+  const __bf16* qh = q + qoff;
+  const __bf16* doh = d_o + qoff;
+  const float* lseh = lse + ((size_t)b * Hq + (size_t)hk * G) * Lq;   // head g at + g * Lq
+  const float* dlh = delta + ((size_t)b * Hq + (size_t)hk * G) * Lq;
   const int key = kb * 128 + 32 * pw + l32;
 
   const int qstart = CAUSAL ? kb * 128 : 0;
-  const int nqt = (L - qstart + BQ - 1) / BQ;
+  const int nqt = (Lq - qstart + BQ - 1) / BQ;   // query tiles per query head
+  const int nsteps = G * nqt;
   // under the causal mask only the first two query tiles reach above a key of this block
   const int nmask = CAUSAL ? min(nqt, 2) : 0;
 
   // staging of Q, dO, lse, delta by the producer waves (threads 0..255) through
-  // buffer loads; rows past the end of the sequence read as zero
+  // buffer loads; rows past the end of the sequence read as zero (the range
+  // covers Lq rows from the group's first head, and every head of the group
+  // lies inside a row)
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
-  const uint32_t head_bytes = (uint32_t)((size_t)L * rs * 2);
+  const uint32_t head_bytes = (uint32_t)((size_t)Lq * rsq * 2);
   const __amdgpu_buffer_rsrc_t qrs = head_rsrc(qh, head_bytes);
   const __amdgpu_buffer_rsrc_t drs = head_rsrc(doh, head_bytes);
   uint32_t voff[CH];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rs + scol) * 2);
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsq + scol) * 2);
   u32x4 qreg[CH], dreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
-  auto load_tile = [&](int qt) {
-    const uint32_t soff = (uint32_t)(qstart + qt * BQ) * (uint32_t)(rs * 2);
+  // step t handles query tile t mod nqt of the group's query head t div nqt
+  const FastDiv fq = make_fastdiv((uint32_t)nqt);
+  auto load_tile = [&](int t) {
+    const int g = (int)fdiv((uint32_t)t, fq), qt = t - g * nqt;
+    const uint32_t soff = (uint32_t)(qstart + qt * BQ) * (uint32_t)(rsq * 2) + (uint32_t)(g * D * 2);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       qreg[j] = buf_load16(qrs, voff[j] + soff, 0);
@@ -124,8 +138,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     if (tid < BQ) {
       const int qi = qstart + qt * BQ + tid;
       // rows past the end get lse = +inf, so their probabilities are exactly 0
-      lse_r = qi < L ? lseh[qi] * kLog2e : INFINITY;
-      dl_r = qi < L ? dlh[qi] : 0.f;
+      lse_r = qi < Lq ? lseh[(size_t)g * Lq + qi] * kLog2e : INFINITY;
+      dl_r = qi < Lq ? dlh[(size_t)g * Lq + qi] : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -145,17 +159,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     bf16x8 kf[KS], vf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (key < L) {
-        kf[ks] = *reinterpret_cast<const bf16x8*>(k + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
-        vf[ks] = *reinterpret_cast<const bf16x8*>(v + head_off + (size_t)key * rs + 16 * ks + 8 * hl);
+      if (key < Lk) {
+        kf[ks] = *reinterpret_cast<const bf16x8*>(k + koff + (size_t)key * rsk + 16 * ks + 8 * hl);
+        vf[ks] = *reinterpret_cast<const bf16x8*>(v + koff + (size_t)key * rsk + 16 * ks + 8 * hl);
       } else {
         kf[ks] = bf16x8{};
         vf[ks] = bf16x8{};
       }
     }
-    auto produce = [&](int qt, auto mask_tag) {
+    // step s (LDS buffer s & 1) handles query tile qt of one query head
+    auto produce = [&](int s, int qt, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      const int cur = qt & 1;
+      const int cur = s & 1;
       const int q0 = qstart + qt * BQ;
       const __bf16* Qc = Qs[cur];
       const __bf16* Dc = Ds[cur];
@@ -200,15 +215,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     load_tile(0);
     store_tile(0);
     __syncthreads();
-    if (nqt > 1) load_tile(1);
-    for (int s = 0; s <= nqt; ++s) {
-      if (s < nmask)
-        produce(s, std::integral_constant<bool, true>{});
-      else if (s < nqt)
-        produce(s, std::integral_constant<bool, false>{});
+    if (nsteps > 1) load_tile(1);
+    for (int s = 0; s <= nsteps; ++s) {
+      if (s < nsteps) {
+        const int qt = s - (int)fdiv((uint32_t)s, fq) * nqt;
+        if (CAUSAL && qt < nmask)
+          produce(s, qt, std::integral_constant<bool, true>{});
+        else
+          produce(s, qt, std::integral_constant<bool, false>{});
+      }
       __syncthreads();  // hand-over of tile s; consumers are done with tile s-1's buffers
-      if (s + 1 < nqt) store_tile((s + 1) & 1);
-      if (s + 2 < nqt) load_tile(s + 2);
+      if (s + 1 < nsteps) store_tile((s + 1) & 1);
+      if (s + 2 < nsteps) load_tile(s + 2);
       __syncthreads();  // tile s+1 staged
     }
   } else {
@@ -220,7 +238,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       dvacc[dt] = f32x16{};
     }
     __syncthreads();  // tile 0 staged
-    for (int s = 0; s <= nqt; ++s) {
+    for (int s = 0; s <= nsteps; ++s) {
       if (s >= 1) {
         const int prev = (s - 1) & 1;
         const __bf16* Qc = Qs[prev];
@@ -239,9 +257,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       __syncthreads();
       __syncthreads();
     }
-    if (key < L) {
-      __bf16* dkrow = dk + head_off + (size_t)key * rs;
-      __bf16* dvrow = dv + head_off + (size_t)key * rs;
+    if (key < Lk) {
+      __bf16* dkrow = dk + koff + (size_t)key * rsk;
+      __bf16* dvrow = dv + koff + (size_t)key * rsk;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -258,7 +276,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dq, int L, int Hh, int nqb, int nhb, float sl2, float scale) {
+    __bf16* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale) {
   constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256, RSTEP = 256 / CPR;
   constexpr int KST = Stride<D>::both;  // K: rows for S^T = K Q^T, transposed for dQ^T += K^T dS^T
   constexpr int VST = Stride<D>::row;   // V: rows for dP^T = V dO^T
@@ -268,45 +286,46 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = nqb - 1 - (int)blockIdx.x / nhb;
-  const int hb = blockIdx.x % nhb;
-  const int b = hb / Hh, h = hb - b * Hh;
-  const size_t rs = (size_t)Hh * D;
-  const size_t head_off = ((size_t)b * L * Hh + h) * D;
-  const __bf16* kh = k + head_off;
-  const __bf16* vh = v + head_off;
+  const int hb = blockIdx.x % nhb;         // (batch, query head) pair
+  const int b = hb / Hq, h = hb - b * Hq;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
+  const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
+  const __bf16* kh = k + koff;
+  const __bf16* vh = v + koff;
   const int q0 = qb * BM;
   const int qw0 = q0 + 32 * wave;
   const int qrow = qw0 + l32;
-  const bool valid = qrow < L;
+  const bool valid = qrow < Lq;
 
   bf16x8 qf[KS], df[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (valid) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(q + head_off + (size_t)qrow * rs + 16 * ks + 8 * hl);
-      df[ks] = *reinterpret_cast<const bf16x8*>(d_o + head_off + (size_t)qrow * rs + 16 * ks + 8 * hl);
+      qf[ks] = *reinterpret_cast<const bf16x8*>(q + qoff + (size_t)qrow * rsq + 16 * ks + 8 * hl);
+      df[ks] = *reinterpret_cast<const bf16x8*>(d_o + qoff + (size_t)qrow * rsq + 16 * ks + 8 * hl);
     } else {
       qf[ks] = bf16x8{};
       df[ks] = bf16x8{};
     }
   }
-  const float nlse2 = valid ? -lse[(size_t)hb * L + qrow] * kLog2e : 0.f;
-  const float dl = valid ? delta[(size_t)hb * L + qrow] : 0.f;
+  const float nlse2 = valid ? -lse[(size_t)hb * Lq + qrow] * kLog2e : 0.f;
+  const float dl = valid ? delta[(size_t)hb * Lq + qrow] : 0.f;
 
   f32x16 dqacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dqacc[dt] = f32x16{};
 
-  const int kend = CAUSAL ? min(L, q0 + BM) : L;
+  const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int nkb = (kend + BN - 1) / BN;
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
-  const uint32_t head_bytes = (uint32_t)((size_t)L * rs * 2);
+  const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vh, head_bytes);
   uint32_t voff[CH];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rs + scol) * 2);
-  const uint32_t tile_bytes = (uint32_t)(BN * rs * 2);
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsk + scol) * 2);
+  const uint32_t tile_bytes = (uint32_t)(BN * rsk * 2);
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int kb) {
     const uint32_t soff = (uint32_t)kb * tile_bytes;
@@ -330,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* Kc = Ks[cur];
     const __bf16* Vc = Vs[cur];
     const int k0 = kb * BN;
-    const bool edge = EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > L));
+    const bool edge = EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk));
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -348,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int kk = k0 + 32 * mt + 8 * (e >> 2) + 4 * hl + (e & 3);
-          if (CAUSAL ? (kk > qrow) : (kk >= L)) s[e] = 0.f;
+          if (CAUSAL ? (kk > qrow) : (kk >= Lk)) s[e] = 0.f;
         }
       }
 #pragma unroll
@@ -369,13 +388,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   __syncthreads();
   if (nkb > 1) load_tile(1);
   // as in the forward pass: only the last two key tiles (causal) or a ragged last tile need a mask
-  const int nsteady = CAUSAL ? max(0, nkb - 2) : (L % BN ? nkb - 1 : nkb);
+  const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
   int kb = 0;
   for (; kb < nsteady; ++kb) tile(kb, std::integral_constant<bool, false>{});
   for (; kb < nkb; ++kb) tile(kb, std::integral_constant<bool, true>{});
 
   if (valid) {
-    __bf16* row = dq + head_off + (size_t)qrow * rs;
+    __bf16* row = dq + qoff + (size_t)qrow * rsq;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -390,64 +409,69 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dk, float* __restrict__ dv, int L, int Hh, int nhb, float scale) {
+    float* __restrict__ dk, float* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float scale) {
   constexpr int BQ = 32;
   __shared__ float Qs[BQ][D];
   __shared__ float Os[BQ][D];
   __shared__ float ls[BQ], dls[BQ];
   const int tid = threadIdx.x;
   const int kb = blockIdx.x / nhb;
-  const int hb = blockIdx.x % nhb;
-  const int b = hb / Hh, h = hb - b * Hh;
-  const size_t rs = (size_t)Hh * D;
-  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const int hb = blockIdx.x % nhb;         // (batch, key head) pair
+  const int b = hb / Hk, hk = hb - b * Hk;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
+  const size_t koff = ((size_t)b * Lk * Hk + hk) * D;
   const int key = kb * 64 + tid;
-  const bool valid = key < L;
+  const bool valid = key < Lk;
   float kv[D], vv[D], dka[D], dva[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    kv[e] = valid ? k[head_off + (size_t)key * rs + e] : 0.f;
-    vv[e] = valid ? v[head_off + (size_t)key * rs + e] : 0.f;
+    kv[e] = valid ? k[koff + (size_t)key * rsk + e] : 0.f;
+    vv[e] = valid ? v[koff + (size_t)key * rsk + e] : 0.f;
     dka[e] = 0.f;
     dva[e] = 0.f;
   }
   const int qstart = CAUSAL ? kb * 64 : 0;
-  for (int q0 = qstart; q0 < L; q0 += BQ) {
-    __syncthreads();
-    for (int c = tid; c < BQ * D; c += 64) {
-      const int r = c / D, e = c % D, qi = q0 + r;
-      Qs[r][e] = qi < L ? q[head_off + (size_t)qi * rs + e] : 0.f;
-      Os[r][e] = qi < L ? d_o[head_off + (size_t)qi * rs + e] : 0.f;
-    }
-    if (tid < BQ) {
-      const int qi = q0 + tid;
-      ls[tid] = qi < L ? lse[(size_t)hb * L + qi] : 0.f;
-      dls[tid] = qi < L ? delta[(size_t)hb * L + qi] : 0.f;
-    }
-    __syncthreads();
-    const int rn = min(BQ, L - q0);
-    for (int r = 0; r < rn; ++r) {
-      if (CAUSAL && q0 + r < key) continue;
-      float s = 0.f, dp = 0.f;
-#pragma unroll
-      for (int e = 0; e < D; ++e) {
-        s = fmaf(Qs[r][e], kv[e], s);
-        dp = fmaf(Os[r][e], vv[e], dp);
+  for (int g = 0; g < G; ++g) {
+    const int h = hk * G + g;
+    const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+    const size_t loff = ((size_t)b * Hq + h) * Lq;
+    for (int q0 = qstart; q0 < Lq; q0 += BQ) {
+      __syncthreads();
+      for (int c = tid; c < BQ * D; c += 64) {
+        const int r = c / D, e = c % D, qi = q0 + r;
+        Qs[r][e] = qi < Lq ? q[qoff + (size_t)qi * rsq + e] : 0.f;
+        Os[r][e] = qi < Lq ? d_o[qoff + (size_t)qi * rsq + e] : 0.f;
       }
-      const float p = expf(s * scale - ls[r]);
-      const float ds = p * (dp - dls[r]);
+      if (tid < BQ) {
+        const int qi = q0 + tid;
+        ls[tid] = qi < Lq ? lse[loff + qi] : 0.f;
+        dls[tid] = qi < Lq ? delta[loff + qi] : 0.f;
+      }
+      __syncthreads();
+      const int rn = min(BQ, Lq - q0);
+      for (int r = 0; r < rn; ++r) {
+        if (CAUSAL && q0 + r < key) continue;
+        float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int e = 0; e < D; ++e) {
-        dva[e] = fmaf(p, Os[r][e], dva[e]);
-        dka[e] = fmaf(ds, Qs[r][e], dka[e]);
+        for (int e = 0; e < D; ++e) {
+          s = fmaf(Qs[r][e], kv[e], s);
+          dp = fmaf(Os[r][e], vv[e], dp);
+        }
+        const float p = expf(s * scale - ls[r]);
+        const float ds = p * (dp - dls[r]);
+#pragma unroll
+        for (int e = 0; e < D; ++e) {
+          dva[e] = fmaf(p, Os[r][e], dva[e]);
+          dka[e] = fmaf(ds, Qs[r][e], dka[e]);
+        }
       }
     }
   }
   if (valid) {
 #pragma unroll
     for (int e = 0; e < D; ++e) {
-      dk[head_off + (size_t)key * rs + e] = dka[e] * scale;
-      dv[head_off + (size_t)key * rs + e] = dva[e];
+      dk[koff + (size_t)key * rsk + e] = dka[e] * scale;
+      dv[koff + (size_t)key * rsk + e] = dva[e];
     }
   }
 }
@@ -457,37 +481,38 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dq, int L, int Hh, int nqb, int nhb, float scale) {
+    float* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float scale) {
   constexpr int BN = 32;
   __shared__ float Ks[BN][D];
   __shared__ float Vs[BN][D];
   const int tid = threadIdx.x;
   const int qb = nqb - 1 - (int)blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;
-  const int b = hb / Hh, h = hb - b * Hh;
-  const size_t rs = (size_t)Hh * D;
-  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const int b = hb / Hq, h = hb - b * Hq;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
+  const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
   const int qrow = qb * 64 + tid;
-  const bool valid = qrow < L;
+  const bool valid = qrow < Lq;
   float qv[D], dov[D], dqa[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    qv[e] = valid ? q[head_off + (size_t)qrow * rs + e] : 0.f;
-    dov[e] = valid ? d_o[head_off + (size_t)qrow * rs + e] : 0.f;
+    qv[e] = valid ? q[qoff + (size_t)qrow * rsq + e] : 0.f;
+    dov[e] = valid ? d_o[qoff + (size_t)qrow * rsq + e] : 0.f;
     dqa[e] = 0.f;
   }
-  const float l_i = valid ? lse[(size_t)hb * L + qrow] : 0.f;
-  const float d_i = valid ? delta[(size_t)hb * L + qrow] : 0.f;
-  const int kend = CAUSAL ? min(L, qb * 64 + 64) : L;
+  const float l_i = valid ? lse[(size_t)hb * Lq + qrow] : 0.f;
+  const float d_i = valid ? delta[(size_t)hb * Lq + qrow] : 0.f;
+  const int kend = CAUSAL ? min(Lk, qb * 64 + 64) : Lk;
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
     for (int c = tid; c < BN * D; c += 64) {
       const int r = c / D, e = c % D, kk = k0 + r;
-      Ks[r][e] = kk < L ? k[head_off + (size_t)kk * rs + e] : 0.f;
-      Vs[r][e] = kk < L ? v[head_off + (size_t)kk * rs + e] : 0.f;
+      Ks[r][e] = kk < Lk ? k[koff + (size_t)kk * rsk + e] : 0.f;
+      Vs[r][e] = kk < Lk ? v[koff + (size_t)kk * rsk + e] : 0.f;
     }
     __syncthreads();
-    const int jn = min(BN, L - k0);
+    const int jn = min(BN, Lk - k0);
     for (int j = 0; j < jn; ++j) {
       if (CAUSAL && k0 + j > qrow) break;
       float s = 0.f, dp = 0.f;
@@ -504,16 +529,16 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
   }
   if (valid) {
 #pragma unroll
-    for (int e = 0; e < D; ++e) dq[head_off + (size_t)qrow * rs + e] = dqa[e] * scale;
+    for (int e = 0; e < D; ++e) dq[qoff + (size_t)qrow * rsq + e] = dqa[e] * scale;
   }
 }
 
 template <typename T, int D>
 hipError_t launch_delta(const T* o, const T* d_o, float* delta, const AttnShape& s, hipStream_t stream) {
-  const int rows = s.B * s.L * s.Hh;
+  const int rows = s.B * s.Lq * s.Hq;
   const long long threads = (long long)rows * (D / 8);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, o, d_o, delta, s.L, s.Hh, rows);
+  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, o, d_o, delta, s.Lq, s.Hq, rows);
   return hipGetLastError();
 }
 
@@ -522,19 +547,21 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
                     void* dq, void* dk, void* dv, float* delta, const AttnShape& s, hipStream_t stream) {
   hipError_t e = launch_delta<__bf16, D>((const __bf16*)o, (const __bf16*)d_o, delta, s, stream);
   if (e != hipSuccess) return e;
-  const int nhb = s.B * s.Hh;
+  const int G = s.Hq / s.Hk;
   const float scale = 1.f / sqrtf((float)D);
   const float sl2 = scale * kLog2e;
-  const int nkb = (s.L + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)nkb * nhb), dim3(512), 0, stream,
+  const int nkhb = s.B * s.Hk;
+  const int nkb = (s.Lk + 127) / 128;
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                     (__bf16*)dk, (__bf16*)dv, s.L, s.Hh, nhb, sl2, scale);
+                     (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nqb = (s.L + 127) / 128;
+  const int nhb = s.B * s.Hq;
+  const int nqb = (s.Lq + 127) / 128;
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                     (__bf16*)dq, s.L, s.Hh, nqb, nhb, sl2, scale);
+                     (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale);
   return hipGetLastError();
 }
 
@@ -544,22 +571,25 @@ hipError_t bwd_f32(const float* q, const float* k, const float* v, const float* 
                    hipStream_t stream) {
   hipError_t e = launch_delta<float, D>(o, d_o, delta, s, stream);
   if (e != hipSuccess) return e;
-  const int nhb = s.B * s.Hh;
+  const int G = s.Hq / s.Hk;
   const float scale = 1.f / sqrtf((float)D);
-  const int nb = (s.L + 63) / 64;
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)nb * nhb), dim3(64), 0, stream, q, k, v, d_o,
-                     lse, delta, dk, dv, s.L, s.Hh, nhb, scale);
+  const int nkhb = s.B * s.Hk;
+  const int nkb = (s.Lk + 63) / 64;
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)nkb * nkhb), dim3(64), 0, stream, q, k, v,
+                     d_o, lse, delta, dk, dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)nb * nhb), dim3(64), 0, stream, q, k, v, d_o,
-                     lse, delta, dq, s.L, s.Hh, nb, nhb, scale);
+  const int nhb = s.B * s.Hq;
+  const int nqb = (s.Lq + 63) / 64;
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(64), 0, stream, q, k, v,
+                     d_o, lse, delta, dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(const AttnShape& s) {
-  const size_t delta = (size_t)s.B * s.Hh * s.L * sizeof(float);
+  const size_t delta = (size_t)s.B * s.Hq * s.Lq * sizeof(float);
   return (delta + 255) / 256 * 256;
 }
 

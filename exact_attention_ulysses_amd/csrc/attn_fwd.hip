@@ -18,6 +18,10 @@
 //   walk; the next K/V tile is loaded into registers while the current one is
 //   used from LDS. Causal query blocks are dispatched longest first and never
 //   visit key blocks above the diagonal.
+// Grouped-query attention (pinyu.ai, section "Head-count constraints"): the
+//   key/value buffers may hold fewer heads than the query buffer; query head h
+//   reads key head h / G. Queries and keys may have different lengths
+//   (cross-attention, papers.chlience.com note, section 5.4; bidirectional only).
 // fp32 path: one lane per query row, K/V tiles in LDS, plain FMAs (used for
 //   the small fp32 workloads; precision reference for the tests).
 #include <math.h>
@@ -38,7 +42,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int L, int Hh, int nqb, int nhb, float sl2) {
+    __bf16* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
+    float sl2) {
   constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CH = BN * CPR / 256;         // chunks per thread per tile
@@ -52,13 +57,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / nhb;  // longest rows first
-  const int hb = bid % nhb;            // (batch, head) pair
-  const int b = hb / Hh, h = hb - b * Hh;
-  const size_t rs = (size_t)Hh * D;
-  const size_t head_off = ((size_t)b * L * Hh + h) * D;
-  const __bf16* qh = q + head_off;
-  const __bf16* kh = k + head_off;
-  const __bf16* vh = v + head_off;
+  const int hb = bid % nhb;            // (batch, query head) pair
+  const int b = hb / Hq, h = hb - b * Hq;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;   // row strides
+  const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
+  const __bf16* qh = q + qoff;
+  const __bf16* kh = k + koff;
+  const __bf16* vh = v + koff;
   const int q0 = qb * BM;
   const int qw0 = q0 + 32 * wave;      // first query row of this wave
   const int qrow = qw0 + l32;
@@ -67,8 +73,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (qrow < L)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * rs + 16 * ks + 8 * hl);
+    if (qrow < Lq)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * rsq + 16 * ks + 8 * hl);
     else
       qf[ks] = bf16x8{};
   }
@@ -79,19 +85,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   // running maximum in log2 units and this lane's share of the running sum
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kend = CAUSAL ? min(L, q0 + BM) : L;
+  const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int nkb = (kend + BN - 1) / BN;
 
   // staging: thread tid moves chunks of rows srow + j * RSTEP, columns scol .. scol+7,
   // through buffer loads (constant per-lane offset, scalar tile offset)
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
-  const uint32_t head_bytes = (uint32_t)((size_t)L * rs * 2);
+  const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vh, head_bytes);
   uint32_t voff[CH];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rs + scol) * 2);
-  const uint32_t tile_bytes = (uint32_t)(BN * rs * 2);
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsk + scol) * 2);
+  const uint32_t tile_bytes = (uint32_t)(BN * rsk * 2);
   u32x4 kreg[CH], vreg[CH];
   auto load_tile = [&](int kb) {
     const uint32_t soff = (uint32_t)kb * tile_bytes;
@@ -126,12 +132,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
     }
 
-    if (EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > L))) {
+    if (EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk))) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
-        if (CAUSAL ? (key > qrow) : (key >= L)) s0[e] = -INFINITY;
-        if (CAUSAL ? (key + 32 > qrow) : (key + 32 >= L)) s1[e] = -INFINITY;
+        if (CAUSAL ? (key > qrow) : (key >= Lk)) s0[e] = -INFINITY;
+        if (CAUSAL ? (key + 32 > qrow) : (key + 32 >= Lk)) s1[e] = -INFINITY;
       }
     }
 
@@ -184,22 +190,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   if (nkb > 1) load_tile(1);
   // causal: only the last two key tiles reach above a query row of this block;
   // otherwise only a ragged last tile holds keys past the end
-  const int nsteady = CAUSAL ? max(0, nkb - 2) : (L % BN ? nkb - 1 : nkb);
+  const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
   int kb = 0;
   for (; kb < nsteady; ++kb) tile(kb, std::integral_constant<bool, false>{});
   for (; kb < nkb; ++kb) tile(kb, std::integral_constant<bool, true>{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
-  if (qrow < L) {
-    __bf16* orow = o + head_off + (size_t)qrow * rs;
+  if (qrow < Lq) {
+    __bf16* orow = o + qoff + (size_t)qrow * rsq;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
     }
-    if (hl == 0) lse[(size_t)hb * L + qrow] = (m_run + log2f(l_tot)) * kLn2;
+    if (hl == 0) lse[(size_t)hb * Lq + qrow] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -207,36 +213,38 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int L, int Hh, int nqb, int nhb, float scale) {
+    float* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
+    float scale) {
   constexpr int BN = 32;
   __shared__ float Ks[BN][D];
   __shared__ float Vs[BN][D];
   const int tid = threadIdx.x;
   const int qb = nqb - 1 - (int)blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;
-  const int b = hb / Hh, h = hb - b * Hh;
-  const size_t rs = (size_t)Hh * D;
-  const size_t head_off = ((size_t)b * L * Hh + h) * D;
+  const int b = hb / Hq, h = hb - b * Hq;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
+  const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
   const int qrow = qb * 64 + tid;
-  const bool valid = qrow < L;
+  const bool valid = qrow < Lq;
 
   float qv[D], ov[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    qv[e] = valid ? q[head_off + (size_t)qrow * rs + e] * scale : 0.f;
+    qv[e] = valid ? q[qoff + (size_t)qrow * rsq + e] * scale : 0.f;
     ov[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kend = CAUSAL ? min(L, qb * 64 + 64) : L;
+  const int kend = CAUSAL ? min(Lk, qb * 64 + 64) : Lk;
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
     for (int c = tid; c < BN * D; c += 64) {
       const int r = c / D, e = c % D, key = k0 + r;
-      Ks[r][e] = key < L ? k[head_off + (size_t)key * rs + e] : 0.f;
-      Vs[r][e] = key < L ? v[head_off + (size_t)key * rs + e] : 0.f;
+      Ks[r][e] = key < Lk ? k[koff + (size_t)key * rsk + e] : 0.f;
+      Vs[r][e] = key < Lk ? v[koff + (size_t)key * rsk + e] : 0.f;
     }
     __syncthreads();
-    const int jn = min(BN, L - k0);
+    const int jn = min(BN, Lk - k0);
     for (int j = 0; j < jn; ++j) {
       if (CAUSAL && k0 + j > qrow) break;
       float s = 0.f;
@@ -258,31 +266,31 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
   if (valid) {
     const float inv = 1.f / l;
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[head_off + (size_t)qrow * rs + e] = ov[e] * inv;
-    lse[(size_t)hb * L + qrow] = m + logf(l);
+    for (int e = 0; e < D; ++e) o[qoff + (size_t)qrow * rsq + e] = ov[e] * inv;
+    lse[(size_t)hb * Lq + qrow] = m + logf(l);
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnShape& s,
                     hipStream_t stream) {
-  const int nqb = (s.L + 127) / 128;
-  const int nhb = s.B * s.Hh;
+  const int nqb = (s.Lq + 127) / 128;
+  const int nhb = s.B * s.Hq;
   const float sl2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.L, s.Hh, nqb,
-                     nhb, sl2);
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq, s.Hk,
+                     s.Hq / s.Hk, nqb, nhb, sl2);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, const AttnShape& s,
                    hipStream_t stream) {
-  const int nqb = (s.L + 63) / 64;
-  const int nhb = s.B * s.Hh;
+  const int nqb = (s.Lq + 63) / 64;
+  const int nhb = s.B * s.Hq;
   const float scale = 1.f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(64), 0, stream, q, k, v,
-                     o, lse, s.L, s.Hh, nqb, nhb, scale);
+                     o, lse, s.Lq, s.Lk, s.Hq, s.Hk, s.Hq / s.Hk, nqb, nhb, scale);
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ struct FastDiv {
   uint32_t s;
 };
 
-inline FastDiv make_fastdiv(uint32_t d) {
+__host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
   FastDiv f;
   f.d = d;
   uint32_t s = 0;

@@ -9,17 +9,25 @@ namespace ulysses {
 
 struct PermShape {
   uint32_t P, B, Lp;       // ranks, batch, tokens per rank
-  uint32_t run_bytes;      // H/P * d_h * element size (multiple of 128)
-  uint32_t total_words;    // tensor size in 16-byte words (< 2^31)
+  uint32_t run_bytes;      // local heads * d_h * element size (multiple of 128)
+  uint32_t total_words;    // seq-layout tensor size in 16-byte words (< 2^31)
+  uint32_t rep;            // ranks that receive each head group (1, or P / H_kv for
+                           // replicated K/V heads); the head tensor is rep times larger
 };
 
+// seq_to_head (rep copies of every head group) or head_to_seq (rep must be 1)
 hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, bool seq_to_head,
                                 hipStream_t stream);
+// head_to_seq for gradients of replicated K/V heads: the rep replicas are summed
+// (fp32 accumulation, one rounding to the element type)
+hipError_t launch_kv_grad_reduce(const void* src, void* dst, const PermShape& s, bool bf16, hipStream_t stream);
 
 struct AttnShape {
   int B;        // batch (times ranks when several head groups run at once)
-  int L;        // sequence length
-  int Hh;       // heads in the buffer (H/P)
+  int Lq, Lk;   // query rows and key rows (equal for self-attention; causal needs equal)
+  int Hq;       // heads in the query-side buffers q, o, d_o, dq (and lse, delta)
+  int Hk;       // heads in the key-side buffers k, v, dk, dv; query head h uses
+                // key head h / (Hq / Hk)
   int D;        // head dim (64 or 128)
   bool causal;
 };
@@ -30,7 +38,7 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                                const AttnShape& s, hipStream_t stream);
 
-// workspace layout: delta [B][Hh][L] fp32, then (256-byte aligned) nothing else
+// workspace layout: delta [B][Hq][Lq] fp32, then (256-byte aligned) nothing else
 size_t attn_bwd_workspace_bytes(const AttnShape& s);
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* d_o, const float* lse, void* dq, void* dk, void* dv,

@@ -15,6 +15,13 @@
 // at least 128 contiguous bytes, so every line read and written is a full
 // line. Staging through LDS would add a round trip without making any access
 // wider. Values are never converted; bits are copied as they are.
+//
+// K/V heads of grouped-query attention (pinyu.ai, section "Head-count
+// constraints"): with fewer K/V heads than ranks, every rank receives the one
+// K/V head its query heads share, so each head group goes to rep = P / H_kv
+// consecutive ranks. The same kernel writes each word it reads rep times.
+// The gradient of that gather sums the rep replicas back into their token
+// shards (kv_grad_reduce_kernel): the only arithmetic in this file.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +38,7 @@ struct PermArgs {
   uint32_t total;            // 16-byte words in the tensor
   FastDiv fU, f3, f2, f1;    // source extents: [n0][n1][n2][n3][U]
   uint32_t s0, s1, s2, s3;   // destination strides (words) of source coords i0..i3
+  uint32_t rep, srep;        // copies of each word and the distance between them
 };
 
 __global__ __launch_bounds__(kThreads) void perm_kernel(PermArgs a) {
@@ -54,8 +62,60 @@ __global__ __launch_bounds__(kThreads) void perm_kernel(PermArgs a) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t idx = base + u * kThreads;
-    if (idx < a.total) __builtin_nontemporal_store(val[u], a.dst + dsto[u]);
+    if (idx < a.total) {
+      for (uint32_t j = 0; j < a.rep; ++j) __builtin_nontemporal_store(val[u], a.dst + dsto[u] + j * a.srep);
+    }
   }
+}
+
+// dst [r][b][t][g][w] = sum over j < rep of src [g*rep + j][b][r*Lp + t][w]
+// (one head per rank in src, G = P / rep heads in dst); one thread per
+// destination word, replicas summed in order in fp32.
+struct ReduceArgs {
+  const u32x4* __restrict__ src;
+  u32x4* __restrict__ dst;
+  uint32_t total;            // destination words
+  FastDiv fU, fG, fLp, fB;   // destination extents [P][B][Lp][G][U]
+  uint32_t rep;
+  uint32_t sp, sb, sn;       // source strides (words) of rank, batch, token
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void kv_grad_reduce_kernel(ReduceArgs a) {
+  const uint32_t idx = blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= a.total) return;
+  const uint32_t run = fdiv(idx, a.fU);
+  const uint32_t w = idx - run * a.fU.d;
+  const uint32_t t2 = fdiv(run, a.fG);
+  const uint32_t g = run - t2 * a.fG.d;
+  const uint32_t t3 = fdiv(t2, a.fLp);
+  const uint32_t t = t2 - t3 * a.fLp.d;
+  const uint32_t r = fdiv(t3, a.fB);
+  const uint32_t b = t3 - r * a.fB.d;
+  const u32x4* s = a.src + (g * a.rep) * a.sp + b * a.sb + (r * a.fLp.d + t) * a.sn + w;
+  constexpr int N = BF16 ? 8 : 4;
+  float acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.f;
+  for (uint32_t j = 0; j < a.rep; ++j) {
+    const u32x4 x = s[j * a.sp];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint32_t bits = BF16 ? ((x[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) << 16 : x[i];
+      acc[i] += __uint_as_float(bits);
+    }
+  }
+  u32x4 out;
+  if (BF16) {
+    bf16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (__bf16)acc[i];  // round to nearest even
+    out = __builtin_bit_cast(u32x4, h);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __float_as_uint(acc[i]);
+  }
+  a.dst[idx] = out;
 }
 
 }  // namespace
@@ -69,15 +129,20 @@ hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, 
   a.dst = static_cast<u32x4*>(dst);
   a.total = s.total_words;
   a.fU = make_fastdiv(U);
+  a.rep = 1;
+  a.srep = 0;
   if (seq_to_head) {
-    // source [r][b][t][p][w]  ->  destination [p][b][r][t][w]
+    // source [r][b][t][g][w]  ->  destination [g*rep + j][b][r][t][w], j < rep
+    const uint32_t rank_words = B * P * Lp * U;
     a.f1 = make_fastdiv(B);
     a.f2 = make_fastdiv(Lp);
-    a.f3 = make_fastdiv(P);
+    a.f3 = make_fastdiv(P / s.rep);
     a.s0 = Lp * U;             // r
     a.s1 = P * Lp * U;         // b
     a.s2 = U;                  // t
-    a.s3 = B * P * Lp * U;     // p
+    a.s3 = s.rep * rank_words; // g
+    a.rep = s.rep;
+    a.srep = rank_words;
   } else {
     // source [p][b][r][t][w]  ->  destination [r][b][t][p][w]
     a.f1 = make_fastdiv(B);
@@ -91,6 +156,29 @@ hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, 
   const uint32_t per_block = kThreads * kUnroll;
   const uint32_t blocks = (a.total + per_block - 1) / per_block;
   hipLaunchKernelGGL(perm_kernel, dim3(blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_grad_reduce(const void* src, void* dst, const PermShape& s, bool bf16, hipStream_t stream) {
+  const uint32_t U = s.run_bytes / 16;  // words per (token, head)
+  const uint32_t P = s.P, B = s.B, Lp = s.Lp, G = s.P / s.rep;
+  ReduceArgs a;
+  a.src = static_cast<const u32x4*>(src);
+  a.dst = static_cast<u32x4*>(dst);
+  a.total = s.total_words;
+  a.fU = make_fastdiv(U);
+  a.fG = make_fastdiv(G);
+  a.fLp = make_fastdiv(Lp);
+  a.fB = make_fastdiv(B);
+  a.rep = s.rep;
+  a.sn = U;
+  a.sb = P * Lp * U;
+  a.sp = B * P * Lp * U;
+  const uint32_t blocks = (a.total + kThreads - 1) / kThreads;
+  if (bf16)
+    hipLaunchKernelGGL(kv_grad_reduce_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(kv_grad_reduce_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

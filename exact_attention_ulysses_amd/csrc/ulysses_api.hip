@@ -67,23 +67,142 @@ int perm_entry(const void* src, void* dst, int64_t B, int64_t L, int64_t H, int6
   s.Lp = (uint32_t)(L / P);
   s.run_bytes = (uint32_t)(H / P * d_h * elem_size(dtype));
   s.total_words = (uint32_t)(bytes / 16);
+  s.rep = 1;
   return report(launch_seq_head_perm(src, dst, s, seq_to_head, static_cast<hipStream_t>(stream)));
 }
 
-int attn_dims(int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P, int causal, int dtype, AttnShape* s) {
-  int st = check_dims(B, L, H, d_h, P, dtype);
-  if (st != ULYSSES_OK) return st;
+// K/V heads per rank after the layout change: H_kv / P when the heads split
+// evenly, else 1 (replicated over P / H_kv ranks); 0 when neither divides.
+int64_t kv_local_heads(int64_t Hkv, int64_t P) {
+  if (Hkv % P == 0) return Hkv / P;
+  if (P % Hkv == 0) return 1;
+  return 0;
+}
+
+// K/V layout change (replicating) and its gradient (summing replicas)
+int kv_perm_entry(const void* src, void* dst, int64_t B, int64_t L, int64_t Hkv, int64_t d_h, int64_t P, int dtype,
+                  void* stream, bool seq_to_head) {
+  if (!src || !dst) return ULYSSES_INVALID_ARGUMENT;
+  if (B <= 0 || L <= 0 || Hkv <= 0 || d_h <= 0 || P <= 0) return ULYSSES_INVALID_ARGUMENT;
+  if (!valid_dtype(dtype)) return ULYSSES_UNSUPPORTED;
+  const int64_t Hl = kv_local_heads(Hkv, P);
+  if (Hl == 0 || L % P != 0) return ULYSSES_NOT_DIVISIBLE;
+  if (!valid_head_dim(d_h)) return ULYSSES_UNSUPPORTED;
+  if (B > (int64_t(1) << 30) || L > (int64_t(1) << 30) || Hkv > (int64_t(1) << 20) || P > (int64_t(1) << 20))
+    return ULYSSES_UNSUPPORTED;
+  const int64_t es = elem_size(dtype);
+  const int64_t seq_bytes = B * L * Hkv * d_h * es;
+  const int64_t head_bytes = P * B * L * Hl * d_h * es;   // = seq_bytes * rep
+  if (head_bytes / 16 >= kMaxWords) return ULYSSES_UNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return ULYSSES_MISALIGNED;
+  const int64_t src_bytes = seq_to_head ? seq_bytes : head_bytes;
+  const int64_t dst_bytes = seq_to_head ? head_bytes : seq_bytes;
+  if (overlap(range_of(src, src_bytes), range_of(dst, dst_bytes))) return ULYSSES_ALIASING;
+  PermShape s;
+  s.P = (uint32_t)P;
+  s.B = (uint32_t)B;
+  s.Lp = (uint32_t)(L / P);
+  s.run_bytes = (uint32_t)(Hl * d_h * es);
+  s.total_words = (uint32_t)(seq_bytes / 16);
+  s.rep = (uint32_t)(P * Hl / Hkv);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (seq_to_head || s.rep == 1) return report(launch_seq_head_perm(src, dst, s, seq_to_head, hs));
+  return report(launch_kv_grad_reduce(src, dst, s, dtype == ULYSSES_BF16, hs));
+}
+
+// Attention sizes: B batch, Lq query rows, Lk key rows, Hq / Hkv global query /
+// key-value heads, P ranks; the buffers hold one rank's Hq / P query heads and
+// its K/V heads (kv_local_heads).
+int attn_dims(int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal,
+              int dtype, AttnShape* s) {
+  if (B <= 0 || Lq <= 0 || Lk <= 0 || Hq <= 0 || Hkv <= 0 || d_h <= 0 || P <= 0) return ULYSSES_INVALID_ARGUMENT;
   if (causal != 0 && causal != 1) return ULYSSES_INVALID_ARGUMENT;
-  const int64_t Hh = H / P;
-  if (B * Hh > (int64_t(1) << 24) || B * L * Hh >= (int64_t(1) << 31)) return ULYSSES_UNSUPPORTED;
-  // the kernels address one head's rows (plus a padded last tile) with 32-bit byte offsets
-  if ((L + 256) * Hh * d_h * elem_size(dtype) >= (int64_t(1) << 32)) return ULYSSES_UNSUPPORTED;
+  if (!valid_dtype(dtype)) return ULYSSES_UNSUPPORTED;
+  if (Hq % P != 0 || Hq % Hkv != 0 || kv_local_heads(Hkv, P) == 0) return ULYSSES_NOT_DIVISIBLE;
+  if (!valid_head_dim(d_h)) return ULYSSES_UNSUPPORTED;
+  // the causal mask is defined on a shared token axis (self-attention)
+  if (causal == 1 && Lq != Lk) return ULYSSES_UNSUPPORTED;
+  if (B > (int64_t(1) << 30) || Lq > (int64_t(1) << 30) || Lk > (int64_t(1) << 30) || Hq > (int64_t(1) << 20))
+    return ULYSSES_UNSUPPORTED;
+  const int64_t Hql = Hq / P, Hkl = kv_local_heads(Hkv, P), es = elem_size(dtype);
+  if (B * Hql > (int64_t(1) << 24) || B * Lq * Hql >= (int64_t(1) << 31) || B * Lk * Hkl >= (int64_t(1) << 31))
+    return ULYSSES_UNSUPPORTED;
+  // each tensor below 32 GiB (this also keeps every grid below 2^32 work-items)
+  if (B * Lq * Hql * d_h * es / 16 >= kMaxWords || B * Lk * Hkl * d_h * es / 16 >= kMaxWords)
+    return ULYSSES_UNSUPPORTED;
+  // the kernels address one batch's rows (plus a padded last tile) with 32-bit byte offsets
+  if ((Lq + 256) * Hql * d_h * es >= (int64_t(1) << 32) || (Lk + 256) * Hkl * d_h * es >= (int64_t(1) << 32))
+    return ULYSSES_UNSUPPORTED;
   s->B = (int)B;
-  s->L = (int)L;
-  s->Hh = (int)Hh;
+  s->Lq = (int)Lq;
+  s->Lk = (int)Lk;
+  s->Hq = (int)Hql;
+  s->Hk = (int)Hkl;
   s->D = (int)d_h;
   s->causal = causal == 1;
   return ULYSSES_OK;
+}
+
+int64_t q_bytes(const AttnShape& s, int dtype) { return (int64_t)s.B * s.Lq * s.Hq * s.D * elem_size(dtype); }
+int64_t k_bytes(const AttnShape& s, int dtype) { return (int64_t)s.B * s.Lk * s.Hk * s.D * elem_size(dtype); }
+int64_t lse_bytes(const AttnShape& s) { return (int64_t)s.B * s.Hq * s.Lq * 4; }
+
+int attn_fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Lq,
+                   int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal, int dtype,
+                   void* stream) {
+  if (!q || !k || !v || !o || !lse) return ULYSSES_INVALID_ARGUMENT;
+  AttnShape s;
+  int st = attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s);
+  if (st != ULYSSES_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return ULYSSES_MISALIGNED;
+  const int64_t tq = q_bytes(s, dtype), tk = k_bytes(s, dtype);
+  const Range ro = range_of(o, tq), rl = range_of(lse, lse_bytes(s));
+  const Range rin[3] = {range_of(q, tq), range_of(k, tk), range_of(v, tk)};
+  for (const Range& r : rin)
+    if (overlap(ro, r) || overlap(rl, r)) return ULYSSES_ALIASING;
+  if (overlap(ro, rl)) return ULYSSES_ALIASING;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dtype == ULYSSES_BF16) return report(launch_attn_fwd_bf16(q, k, v, o, lse, s, hs));
+  return report(launch_attn_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse, s, hs));
+}
+
+size_t attn_ws_entry(int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P,
+                     int causal, int dtype) {
+  AttnShape s;
+  if (attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s) != ULYSSES_OK) return 0;
+  return attn_bwd_workspace_bytes(s);
+}
+
+int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Lq,
+                   int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal, int dtype,
+                   void* stream) {
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv || !workspace) return ULYSSES_INVALID_ARGUMENT;
+  AttnShape s;
+  int st = attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s);
+  if (st != ULYSSES_OK) return st;
+  const void* al16[] = {q, k, v, o, d_o, dq, dk, dv, workspace};
+  for (const void* p : al16)
+    if (!aligned(p, 16)) return ULYSSES_MISALIGNED;
+  if (!aligned(lse, 4)) return ULYSSES_MISALIGNED;
+  const size_t need = attn_bwd_workspace_bytes(s);
+  if (workspace_bytes < need) return ULYSSES_WORKSPACE_TOO_SMALL;
+  const int64_t tq = q_bytes(s, dtype), tk = k_bytes(s, dtype);
+  const Range outs[4] = {range_of(dq, tq), range_of(dk, tk), range_of(dv, tk), range_of(workspace, (int64_t)need)};
+  const Range ins[6] = {range_of(q, tq), range_of(k, tk), range_of(v, tk), range_of(o, tq), range_of(d_o, tq),
+                        range_of(lse, lse_bytes(s))};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return ULYSSES_ALIASING;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return ULYSSES_ALIASING;
+  }
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dtype == ULYSSES_BF16)
+    return report(launch_attn_bwd_bf16(q, k, v, o, d_o, lse, dq, dk, dv, workspace, s, hs));
+  return report(launch_attn_bwd_f32((const float*)q, (const float*)k, (const float*)v, (const float*)o,
+                                    (const float*)d_o, lse, (float*)dq, (float*)dk, (float*)dv, workspace, s, hs));
 }
 
 }  // namespace
@@ -109,62 +228,50 @@ int ulysses_head_to_seq(const void* x_head, void* x_seq, int64_t B, int64_t L, i
   return perm_entry(x_head, x_seq, B, L, H, d_h, P, dtype, stream, false);
 }
 
+int ulysses_seq_to_head_kv(const void* x_seq, void* x_head, int64_t B, int64_t L, int64_t H_kv, int64_t d_h,
+                           int64_t P, int dtype, void* stream) {
+  return kv_perm_entry(x_seq, x_head, B, L, H_kv, d_h, P, dtype, stream, true);
+}
+
+int ulysses_head_to_seq_kv_grad(const void* dx_head, void* dx_seq, int64_t B, int64_t L, int64_t H_kv, int64_t d_h,
+                                int64_t P, int dtype, void* stream) {
+  return kv_perm_entry(dx_head, dx_seq, B, L, H_kv, d_h, P, dtype, stream, false);
+}
+
 int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t L,
                      int64_t H, int64_t d_h, int64_t P, int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return ULYSSES_INVALID_ARGUMENT;
-  AttnShape s;
-  int st = attn_dims(B, L, H, d_h, P, causal, dtype, &s);
-  if (st != ULYSSES_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-    return ULYSSES_MISALIGNED;
-  const int64_t tb = B * L * (H / P) * d_h * elem_size(dtype);
-  const int64_t lb = B * (H / P) * L * 4;
-  const Range ro = range_of(o, tb), rl = range_of(lse, lb);
-  const Range rin[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
-  for (const Range& r : rin)
-    if (overlap(ro, r) || overlap(rl, r)) return ULYSSES_ALIASING;
-  if (overlap(ro, rl)) return ULYSSES_ALIASING;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (dtype == ULYSSES_BF16) return report(launch_attn_fwd_bf16(q, k, v, o, lse, s, hs));
-  return report(launch_attn_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, lse, s, hs));
+  return attn_fwd_entry(q, k, v, o, lse, B, L, L, H, H, d_h, P, causal, dtype, stream);
+}
+
+int ulysses_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t L_q,
+                         int64_t L_kv, int64_t H_q, int64_t H_kv, int64_t d_h, int64_t P, int causal, int dtype,
+                         void* stream) {
+  return attn_fwd_entry(q, k, v, o, lse, B, L_q, L_kv, H_q, H_kv, d_h, P, causal, dtype, stream);
 }
 
 size_t ulysses_attn_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P, int causal,
                                         int dtype) {
-  AttnShape s;
-  if (attn_dims(B, L, H, d_h, P, causal, dtype, &s) != ULYSSES_OK) return 0;
-  return attn_bwd_workspace_bytes(s);
+  return attn_ws_entry(B, L, L, H, H, d_h, P, causal, dtype);
+}
+
+size_t ulysses_attn_bwd_gqa_workspace_bytes(int64_t B, int64_t L_q, int64_t L_kv, int64_t H_q, int64_t H_kv,
+                                            int64_t d_h, int64_t P, int causal, int dtype) {
+  return attn_ws_entry(B, L_q, L_kv, H_q, H_kv, d_h, P, causal, dtype);
 }
 
 int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t L,
                      int64_t H, int64_t d_h, int64_t P, int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv || !workspace) return ULYSSES_INVALID_ARGUMENT;
-  AttnShape s;
-  int st = attn_dims(B, L, H, d_h, P, causal, dtype, &s);
-  if (st != ULYSSES_OK) return st;
-  const void* al16[] = {q, k, v, o, d_o, dq, dk, dv, workspace};
-  for (const void* p : al16)
-    if (!aligned(p, 16)) return ULYSSES_MISALIGNED;
-  if (!aligned(lse, 4)) return ULYSSES_MISALIGNED;
-  const size_t need = attn_bwd_workspace_bytes(s);
-  if (workspace_bytes < need) return ULYSSES_WORKSPACE_TOO_SMALL;
-  const int64_t tb = B * L * (H / P) * d_h * elem_size(dtype);
-  const int64_t lb = B * (H / P) * L * 4;
-  const Range outs[4] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb), range_of(workspace, (int64_t)need)};
-  const Range ins[6] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb), range_of(d_o, tb),
-                        range_of(lse, lb)};
-  for (int i = 0; i < 4; ++i) {
-    for (const Range& r : ins)
-      if (overlap(outs[i], r)) return ULYSSES_ALIASING;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(outs[i], outs[j])) return ULYSSES_ALIASING;
-  }
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (dtype == ULYSSES_BF16)
-    return report(launch_attn_bwd_bf16(q, k, v, o, d_o, lse, dq, dk, dv, workspace, s, hs));
-  return report(launch_attn_bwd_f32((const float*)q, (const float*)k, (const float*)v, (const float*)o,
-                                    (const float*)d_o, lse, (float*)dq, (float*)dk, (float*)dv, workspace, s, hs));
+  return attn_bwd_entry(q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, L, L, H, H, d_h, P, causal,
+                        dtype, stream);
+}
+
+int ulysses_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                         const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t L_q, int64_t L_kv, int64_t H_q, int64_t H_kv, int64_t d_h, int64_t P,
+                         int causal, int dtype, void* stream) {
+  return attn_bwd_entry(q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, L_q, L_kv, H_q, H_kv, d_h,
+                        P, causal, dtype, stream);
 }
 
 const char* ulysses_status_string(int status) {

@@ -13,7 +13,12 @@
  *    item 3 and 3.4.5: per-head scaled dot-product attention, causal or not,
  *    on the full sequence with no communication.
  *  - papers.chlience.com reading note, section 5.1: O'_p = softmax(Q'_p K'_p^T /
- *    sqrt(d_h)) V'_p on rank p's head group.
+ *    sqrt(d_h)) V'_p on rank p's head group; section 5.4: cross-attention
+ *    among the attention kinds the method carries.
+ *  - pinyu.ai, "Head-count constraints", and the aifetchly blog, "Practical
+ *    Deployment Checklist for Long-Context Training": grouped-query / multi-query attention has fewer K/V heads than
+ *    query heads; they split over P ranks when H_kv % P == 0, and otherwise
+ *    each rank holds a replica of the K/V head its query heads use.
  *
  * Conventions shared by every entry point
  *  - Element types: ULYSSES_BF16 (bfloat16) or ULYSSES_FP32. The layout
@@ -40,8 +45,9 @@
  *    ULYSSES_HIP_ERROR; faults inside a kernel surface at the caller's next
  *    synchronisation, as usual for asynchronous work.
  *  - Limits: d_h in {64, 128}; any L >= 1 (partial tiles are masked); each
- *    tensor below 32 GiB; for attention, one head's rows (L * H/P * d_h
- *    elements, plus 256 rows of slack) below 4 GiB, and B * L * H/P < 2^31.
+ *    tensor below 32 GiB; for attention, one batch entry of each tensor (L *
+ *    heads * d_h elements, plus 256 rows of slack) below 4 GiB, and B * L *
+ *    heads < 2^31.
  *    Calls outside these limits return ULYSSES_UNSUPPORTED.
  */
 #ifndef ULYSSES_H
@@ -57,7 +63,7 @@ extern "C" {
 typedef enum ulysses_status {
   ULYSSES_OK = 0,
   ULYSSES_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, bad flag */
-  ULYSSES_NOT_DIVISIBLE = 2,      /* H % P != 0 or L % P != 0 */
+  ULYSSES_NOT_DIVISIBLE = 2,      /* H % P != 0 or L % P != 0 (or a head-count rule of GQA) */
   ULYSSES_UNSUPPORTED = 3,        /* d_h or dtype or size outside what the kernels implement */
   ULYSSES_MISALIGNED = 4,         /* a pointer not 16-byte aligned */
   ULYSSES_ALIASING = 5,           /* an output overlaps an input or another output */
@@ -95,6 +101,36 @@ int ulysses_head_to_seq(const void* x_head, void* x_seq,
                         int dtype, void* stream);
 
 /*
+ * First all-to-all for the K or V tensor of grouped-query attention with H_kv
+ * key/value heads (pinyu.ai, "Head-count constraints"). Let Hl = H_kv / P if
+ * H_kv % P == 0, else Hl = 1 (then P % H_kv must be 0, and R = P / H_kv
+ * consecutive ranks receive the same head). x_seq [P][B][L/P][H_kv][d_h] ->
+ * x_head [P][B][L][Hl][d_h]:
+ *   H_kv % P == 0:  exactly ulysses_seq_to_head with H = H_kv;
+ *   otherwise:      x_head[p][b][r*L/P + t][0][:] = x_seq[r][b][t][p / R][:].
+ * With these K/V heads, rank p's query heads p*H_q/P .. (p+1)*H_q/P - 1 find
+ * their shared K/V head (h / (H_q/H_kv)) locally. x_head is R times the size
+ * of x_seq. Bits are copied unchanged. Not in place. ULYSSES_NOT_DIVISIBLE if
+ * L % P != 0 or neither of H_kv, P divides the other.
+ */
+int ulysses_seq_to_head_kv(const void* x_seq, void* x_head,
+                           int64_t B, int64_t L, int64_t H_kv, int64_t d_h, int64_t P,
+                           int dtype, void* stream);
+
+/*
+ * Gradient of ulysses_seq_to_head_kv (its adjoint): dx_head [P][B][L][Hl][d_h]
+ * -> dx_seq [P][B][L/P][H_kv][d_h]. Without replication this is exactly
+ * ulysses_head_to_seq with H = H_kv (bits copied). With replication the R
+ * replicas of a head are summed:
+ *   dx_seq[r][b][t][g][:] = sum_{j<R} dx_head[g*R + j][b][r*L/P + t][0][:],
+ * accumulated in fp32 in the order j = 0..R-1 and rounded once to `dtype`
+ * (round to nearest even for bf16).
+ */
+int ulysses_head_to_seq_kv_grad(const void* dx_head, void* dx_seq,
+                                int64_t B, int64_t L, int64_t H_kv, int64_t d_h, int64_t P,
+                                int dtype, void* stream);
+
+/*
  * Exact attention on one rank's head group (papers.chlience.com note,
  * section 5.1; paper-graph summary, sections 3.2 and 3.4.5):
  *   O = softmax(Q K^T / sqrt(d_h)) V  per (batch, local head), full length L,
@@ -128,6 +164,40 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /* Workspace ulysses_attn_bwd needs for these sizes (0 if the sizes are invalid). */
 size_t ulysses_attn_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t d_h,
                                         int64_t P, int causal, int dtype);
+
+/*
+ * ulysses_attn_fwd generalised to grouped-query attention and to queries and
+ * keys of different lengths (cross-attention). H_q query heads, H_kv K/V heads
+ * (global counts; H_q % P == 0, H_q % H_kv == 0, and H_kv % P == 0 or
+ * P % H_kv == 0, else ULYSSES_NOT_DIVISIBLE). One rank's buffers:
+ *   q, o   [B][L_q][H_q/P][d_h]       lse [B][H_q/P][L_q] float32
+ *   k, v   [B][L_kv][Hl][d_h]         Hl as in ulysses_seq_to_head_kv
+ * Local query head j uses local K/V head j / (H_q/P / Hl), i.e. global query
+ * head h uses K/V head h / (H_q/H_kv). causal = 1 requires L_q == L_kv
+ * (ULYSSES_UNSUPPORTED otherwise). With H_q == H_kv and L_q == L_kv this is
+ * ulysses_attn_fwd.
+ */
+int ulysses_attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t L_q, int64_t L_kv, int64_t H_q, int64_t H_kv,
+                         int64_t d_h, int64_t P, int causal, int dtype, void* stream);
+
+/*
+ * Gradient of ulysses_attn_fwd_gqa. dq has q's layout; dk, dv have k's, and a
+ * K/V head shared by several query heads receives the sum of their
+ * contributions (accumulated in fp32, rounded once). Workspace as for
+ * ulysses_attn_bwd, sized by ulysses_attn_bwd_gqa_workspace_bytes.
+ */
+int ulysses_attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                         const void* d_o, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int64_t B, int64_t L_q, int64_t L_kv, int64_t H_q, int64_t H_kv,
+                         int64_t d_h, int64_t P, int causal, int dtype, void* stream);
+
+/* Workspace ulysses_attn_bwd_gqa needs for these sizes (0 if the sizes are invalid). */
+size_t ulysses_attn_bwd_gqa_workspace_bytes(int64_t B, int64_t L_q, int64_t L_kv, int64_t H_q,
+                                            int64_t H_kv, int64_t d_h, int64_t P, int causal,
+                                            int dtype);
 
 /* Static, NUL-terminated name of a status code ("ULYSSES_OK", ...). */
 const char* ulysses_status_string(int status);

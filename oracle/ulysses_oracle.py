@@ -412,7 +412,10 @@ def attn_dkv_cols(q, k, v, do, cols: Sequence[int], causal: bool = True,
     Cost O(#rows-that-see-the-columns * L * d); cheap for columns near the end
     of a causal sequence.
     """
-    L, d = k.shape
+    Lk, d = k.shape
+    Lq = q.shape[0]
+    if causal and Lq != Lk:
+        raise ValueError("causal attention needs Lq == Lkv")
     scale = 1.0 / math.sqrt(d)
     cols = np.asarray(sorted(set(int(c) for c in cols)), dtype=np.int64)
     first_row = int(cols.min()) if causal else 0
@@ -420,9 +423,9 @@ def attn_dkv_cols(q, k, v, do, cols: Sequence[int], causal: bool = True,
     dv = np.zeros((len(cols), d))
     kc = np.asarray(k[cols], dtype=np.float64)
     vc = np.asarray(v[cols], dtype=np.float64)
-    for i0 in range(first_row, L, row_block):
-        i1 = min(L, i0 + row_block)
-        nk = _visible_keys(i1, L, causal)
+    for i0 in range(first_row, Lq, row_block):
+        i1 = min(Lq, i0 + row_block)
+        nk = _visible_keys(i1, Lk, causal)
         qb = np.asarray(q[i0:i1], dtype=np.float64)
         dob = np.asarray(do[i0:i1], dtype=np.float64)
         kk = np.asarray(k[:nk], dtype=np.float64)

@@ -126,3 +126,92 @@ def test_python_binding_rejects_mismatched_tensors():
     x = torch.zeros(10)
     with pytest.raises(ValueError):
         U.ulysses_seq_to_head(x, x, 1, 8, 4, 64, 2)   # host tensors are refused before any call
+
+
+def s2h_kv(src, dst, B=1, L=64, Hkv=2, d=128, P=8, dtype=U.BF16):
+    return U.lib().ulysses_seq_to_head_kv(src, dst, B, L, Hkv, d, P, dtype, None)
+
+
+def h2s_kv(src, dst, B=1, L=64, Hkv=2, d=128, P=8, dtype=U.BF16):
+    return U.lib().ulysses_head_to_seq_kv_grad(src, dst, B, L, Hkv, d, P, dtype, None)
+
+
+@pytest.mark.parametrize("fn", [s2h_kv, h2s_kv])
+def test_kv_layout_validation(fn):
+    assert fn(None, A + GB) == 1
+    assert fn(A, A + GB, Hkv=0) == 1
+    assert fn(A, A + GB, Hkv=3, P=2) == 2            # neither divides the other
+    assert fn(A, A + GB, Hkv=4, P=6) == 2
+    assert fn(A, A + GB, L=60, P=8) == 2             # L % P
+    assert fn(A, A + GB, d=80) == 3
+    assert fn(A, A + GB, dtype=5) == 3
+    assert fn(A + 4, A + GB) == 4
+    # the head side is R = P / Hkv = 4 times the seq side: 64*2*128*2 B seq, 4x on the head side
+    seq_bytes, head_bytes = 64 * 2 * 128 * 2, 4 * 64 * 2 * 128 * 2
+    if fn is s2h_kv:
+        assert fn(A + seq_bytes, A) == 5             # destination [A, A+head_bytes) covers the source
+    else:
+        assert fn(A, A + head_bytes - 16) == 5       # source (head side) overlaps destination
+    assert fn(A, A + GB, B=1 << 20, L=1 << 14, Hkv=1, P=16) == 3   # replicated head tensor past 32 GiB
+
+
+def fwd_gqa(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, Lq=1024, Lkv=1024, Hq=32, Hkv=8, d=128,
+            P=8, causal=1, dtype=U.BF16):
+    return U.lib().ulysses_attn_fwd_gqa(q, k, v, o, lse, B, Lq, Lkv, Hq, Hkv, d, P, causal, dtype, None)
+
+
+def test_gqa_forward_validation():
+    for ptr in ("q", "k", "v", "o", "lse"):
+        assert fwd_gqa(**{ptr: None}) == 1, ptr
+    assert fwd_gqa(Lkv=0) == 1
+    assert fwd_gqa(Hkv=0) == 1
+    assert fwd_gqa(Hq=30, Hkv=6, P=8) == 2           # Hq % P
+    assert fwd_gqa(Hq=32, Hkv=6, P=8) == 2           # Hq % Hkv
+    assert fwd_gqa(Hq=48, Hkv=12, P=8) == 2          # neither Hkv % P nor P % Hkv
+    assert fwd_gqa(Lq=1024, Lkv=512) == 3            # causal cross-attention
+    assert fwd_gqa(Lq=1024, Lkv=512, causal=0, d=96) == 3
+    assert fwd_gqa(k=A + GB + 2) == 4
+    # k holds Lkv * Hl * d elements: with Hl = 1 (Hkv = 8, P = 8) that is 256 KiB here
+    assert fwd_gqa(o=A + GB + 4096) == 5             # o overlaps k
+    assert fwd_gqa(o=A + GB + 256 * 1024 - 16) == 5  # o overlaps the last row of k
+    assert fwd_gqa(lse=A + 2 * GB + 64) == 5         # lse overlaps v
+    # shapes validation accepts (the workspace query runs the same checks without launching)
+    ws = U.lib().ulysses_attn_bwd_gqa_workspace_bytes
+    for B, Lq, Lkv, Hq, Hkv, P, causal in ((1, 1000, 3000, 32, 8, 8, 0), (2, 5, 7, 4, 1, 4, 0),
+                                          (1, 64, 64, 64, 2, 16, 1), (1, 64, 64, 8, 8, 8, 1)):
+        assert ws(B, Lq, Lkv, Hq, Hkv, 128, P, causal, U.BF16) > 0
+
+
+def bwd_gqa(ws_bytes=None, B=1, Lq=1024, Lkv=1024, Hq=32, Hkv=2, d=128, P=8, causal=1, dtype=U.BF16, **ptrs):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"]
+    p = {n: A + i * GB for i, n in enumerate(names)}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = U.lib().ulysses_attn_bwd_gqa_workspace_bytes(B, Lq, Lkv, Hq, Hkv, d, P, causal, dtype)
+    return U.lib().ulysses_attn_bwd_gqa(*[p[n] for n in names], ws_bytes, B, Lq, Lkv, Hq, Hkv, d, P, causal,
+                                        dtype, None)
+
+
+def test_gqa_backward_validation():
+    for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert bwd_gqa(**{n: None}) == 1, n
+    assert bwd_gqa(Hkv=3) == 2
+    assert bwd_gqa(Lkv=100) == 3                     # causal needs equal lengths
+    assert bwd_gqa(ws_bytes=64) == 6
+    assert bwd_gqa(dk=A + GB + 512) == 5             # dk overlaps k
+    assert bwd_gqa(dv=A + 7 * GB + 16) == 5          # dv overlaps dk
+    assert bwd_gqa(ws=A + 9 * GB + 8) == 4
+
+
+def test_gqa_workspace_and_reductions():
+    lib = U.lib()
+    # delta [B][Hq/P][Lq] fp32 only: the key side does not change the workspace
+    assert lib.ulysses_attn_bwd_gqa_workspace_bytes(1, 131072, 131072, 32, 8, 128, 8, 1, U.BF16) == 4 * 131072 * 4
+    assert lib.ulysses_attn_bwd_gqa_workspace_bytes(2, 100, 333, 8, 2, 64, 4, 0, U.FP32) == \
+        (2 * 2 * 100 * 4 + 255) // 256 * 256
+    assert lib.ulysses_attn_bwd_gqa_workspace_bytes(1, 100, 333, 8, 2, 64, 4, 1, U.BF16) == 0
+    # with H_q == H_kv and L_q == L_kv the generalised entry points are the plain ones
+    assert lib.ulysses_attn_bwd_gqa_workspace_bytes(1, 4096, 4096, 16, 16, 128, 4, 1, U.BF16) == \
+        lib.ulysses_attn_bwd_workspace_bytes(1, 4096, 16, 128, 4, 1, U.BF16)
+    assert U.kv_local_heads(8, 8) == 1 and U.kv_local_heads(16, 8) == 2
+    assert U.kv_local_heads(2, 8) == 1 and U.kv_local_heads(3, 8) == 0

@@ -15,6 +15,11 @@ output):
   * backward: dQ of the sampled rows (also prefix-checked), dK/dV of sampled
     key columns near the end, and over the full outputs the identities
     sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
+Grouped-query workloads run K and V through the K/V layout change (and dK,
+dV through its gradient form); a K/V head's dK/dV columns are checked
+against the sum of its query heads' oracle columns. The cross-attention
+workload (queries and keys of different lengths) is bidirectional, so it has
+no causal prefix; its dK/dV columns are checked on its first head.
 """
 import gc
 
@@ -25,11 +30,16 @@ import exact_attention_ulysses_amd as U
 import oracle
 from workloads import WORKLOADS, device_tensor, stress_positions
 
-from gpu_common import check_close, to_f64, to_host_bits, torch_mod
+from gpu_common import bf16_ulp, check_close, shared_head_allowed, to_f64, to_host_bits, torch_mod
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["gpt1.2b-L32k-fwd", "gpt7b-L131k", "gpt30b-L262k", "L1m"]
+NAMES = ["gpt1.2b-L32k-fwd", "gpt7b-L131k", "gpt30b-L262k", "L1m", "gqa8-L131k", "gqa2-L131k",
+         "cross-L16k-L131k"]
+
+
+def _kv(n):
+    return n in ("k", "v", "dk", "dv")
 PREFIX = 8192
 
 
@@ -47,30 +57,39 @@ class Run:
     def __init__(self, key):
         torch = torch_mod()
         self.wl = wl = WORKLOADS[key]
-        B, L, H, d, P, Hh = wl.B, wl.L, wl.H, wl.d, wl.P, wl.Hp
+        B, L, H, d, P, Hh, Lk, Hk = wl.B, wl.L, wl.H, wl.d, wl.P, wl.Hp, wl.Lk, wl.Hk
+        self.G = Hh // wl.Hkp      # local query heads per local K/V head
         self.ins = ["q", "k", "v"] + (["do"] if wl.backward else [])
         self.outs = ["o"] + (["dq", "dk", "dv"] if wl.backward else [])
         print(f"[{key}] drawing inputs", flush=True)
         self.seq = {n: device_tensor(wl, n) for n in self.ins}
         self.head = {}
         for n in self.ins:
-            self.head[n] = torch.empty(wl.head_shape, dtype=torch.bfloat16, device="cuda")
-            U.ulysses_seq_to_head(self.seq[n], self.head[n], B, L, H, d, P)
+            self.head[n] = torch.empty(wl.shape_of("fill_d" + n if _kv(n) else "fill_o"), dtype=torch.bfloat16,
+                                       device="cuda")
+            if _kv(n):
+                U.ulysses_seq_to_head_kv(self.seq[n], self.head[n], B, Lk, Hk, d, P)
+            else:
+                U.ulysses_seq_to_head(self.seq[n], self.head[n], B, L, H, d, P)
         self.ohead = {n: device_tensor(wl, "fill_" + n) for n in self.outs}
         r0 = {n: self.head[n][0] for n in self.ins}
         o0 = {n: self.ohead[n][0] for n in self.outs}
         self.lse = torch.empty((B, Hh, L), dtype=torch.float32, device="cuda")
         print(f"[{key}] attention", flush=True)
-        U.ulysses_attn_fwd(r0["q"], r0["k"], r0["v"], o0["o"], self.lse, B, L, H, d, P, wl.causal)
+        U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], self.lse, B, L, Lk, H, Hk, d, P, wl.causal)
         if wl.backward:
-            ws = torch.empty(U.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, wl.causal), dtype=torch.uint8,
-                             device="cuda")
-            U.ulysses_attn_bwd(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], self.lse, o0["dq"], o0["dk"],
-                               o0["dv"], ws, B, L, H, d, P, wl.causal)
+            ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, wl.causal),
+                             dtype=torch.uint8, device="cuda")
+            U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], self.lse, o0["dq"], o0["dk"],
+                                   o0["dv"], ws, B, L, Lk, H, Hk, d, P, wl.causal)
         self.oseq = {}
         for n in self.outs:
-            self.oseq[n] = torch.empty(wl.seq_shape, dtype=torch.bfloat16, device="cuda")
-            U.ulysses_head_to_seq(self.ohead[n], self.oseq[n], B, L, H, d, P)
+            self.oseq[n] = torch.empty(wl.shape_of(n[1:] if _kv(n) else "q"), dtype=torch.bfloat16,
+                                       device="cuda")
+            if _kv(n):
+                U.ulysses_head_to_seq_kv_grad(self.ohead[n], self.oseq[n], B, Lk, Hk, d, P)
+            else:
+                U.ulysses_head_to_seq(self.ohead[n], self.oseq[n], B, L, H, d, P)
         torch.cuda.synchronize()
         print(f"[{key}] device pass done", flush=True)
         self._f64 = {}
@@ -83,10 +102,13 @@ class Run:
         return self._host[n]
 
     def oracle_head(self, n):
-        """Rank 0's head block of input n, [B, L, Hh, d] float64, via the oracle's own layout change."""
+        """Rank 0's head block of input n, [B, L, heads, d] float64, via the oracle's own layout change."""
         if n not in self._f64:
             wl = self.wl
-            bits = oracle.seq_to_head_part(self.host_seq(n), wl.B, wl.L, wl.H, wl.d, wl.P, 0)
+            if _kv(n):
+                bits = oracle.seq_to_head_kv(self.host_seq(n), wl.B, wl.Lk, wl.Hk, wl.d, wl.P)[0]
+            else:
+                bits = oracle.seq_to_head_part(self.host_seq(n), wl.B, wl.L, wl.H, wl.d, wl.P, 0)
             self._f64[n] = oracle.bf16_bits_to_f64(bits)
             gc.collect()
         return self._f64[n]
@@ -126,19 +148,44 @@ def uniform_rows(wl, head, n=24):
 def test_seq_to_head_and_back_bit_exact(key):
     run = get_run(key)
     wl = run.wl
-    B, L, H, d, P = wl.B, wl.L, wl.H, wl.d, wl.P
+    B, L, H, d, P, Lk, Hk = wl.B, wl.L, wl.H, wl.d, wl.P, wl.Lk, wl.Hk
     rng = np.random.default_rng(5)
     ranks = sorted({0, P - 1, int(rng.integers(1, P))})
     for n in run.ins:
         host = run.host_seq(n)
-        for p in ranks:
-            np.testing.assert_array_equal(to_host_bits(run.head[n][p]),
-                                          oracle.seq_to_head_part(host, B, L, H, d, P, p))
+        if _kv(n):
+            want = oracle.seq_to_head_kv(host, B, Lk, Hk, d, P)
+            for p in ranks:
+                np.testing.assert_array_equal(to_host_bits(run.head[n][p]), want[p])
+            del want
+        else:
+            for p in ranks:
+                np.testing.assert_array_equal(to_host_bits(run.head[n][p]),
+                                              oracle.seq_to_head_part(host, B, L, H, d, P, p))
     # head_to_seq of the outputs (rank 0's head block from attention, the other blocks filler)
     for n in run.outs[:2]:
         y = to_host_bits(run.ohead[n])
         for r in ranks:
             np.testing.assert_array_equal(to_host_bits(run.oseq[n][r]), oracle.head_to_seq_part(y, B, L, H, d, P, r))
+        del y
+        gc.collect()
+    # the gradient form of the K/V layout change (bits copied, or replicas summed)
+    if wl.backward:
+        y = to_host_bits(run.ohead["dk"])
+        R = P * wl.Hkp // Hk
+        if R == 1:
+            for r in ranks:
+                np.testing.assert_array_equal(to_host_bits(run.oseq["dk"][r]),
+                                              oracle.head_to_seq_part(y, B, Lk, Hk, d, P, r))
+        else:
+            yf = oracle.bf16_bits_to_f64(y)
+            want = oracle.head_to_seq_kv_grad(yf, B, Lk, Hk, d, P)
+            mag = oracle.head_to_seq_kv_grad(np.abs(yf), B, Lk, Hk, d, P)
+            del yf
+            acc = (R - 1) * 2.0 ** -24 * mag
+            got = to_f64(run.oseq["dk"], "bf16")
+            assert np.all(np.abs(got - want) <= 0.5 * bf16_ulp(np.abs(want) + acc) + acc)
+            del want, mag, got
         del y
         gc.collect()
 
@@ -151,41 +198,56 @@ def test_forward_sampled_rows(key):
     o = to_f64(run.ohead["o"][0], "bf16")
     lse = run.lse.cpu().numpy()
     for h in range(wl.Hp):
+        j = h // run.G
         for kind, rows in (("edge", edge_rows(wl, h)), ("uniform", uniform_rows(wl, h))):
-            ref = oracle.attn_rows(q[0, :, h], k[0, :, h], v[0, :, h], rows, wl.causal)
+            ref = oracle.attn_rows(q[0, :, h], k[0, :, j], v[0, :, j], rows, wl.causal)
             check_close(f"O {kind} rows head {h}", o[0, rows, h], ref["o"], "bf16", fro=(kind == "uniform"))
             assert np.max(np.abs(lse[0, h, rows] - ref["lse"])) <= 1e-3
 
 
-@pytest.mark.parametrize("key", NAMES)
+@pytest.mark.parametrize("key", [n for n in NAMES if WORKLOADS[n].causal])
 def test_causal_prefix_matches_full_run_and_oracle(key):
     torch = torch_mod()
     run = get_run(key)
     wl = run.wl
-    B, H, d, P, Hh = wl.B, wl.H, wl.d, wl.P, wl.Hp
+    B, H, d, P, Hh, Hk = wl.B, wl.H, wl.d, wl.P, wl.Hp, wl.Hk
     Lp = PREFIX
     r0 = {n: run.head[n][0][:, :Lp] for n in run.ins}   # B = 1: the first Lp rows are contiguous
     assert B == 1 and all(t.is_contiguous() for t in r0.values())
     o = torch.empty((B, Lp, Hh, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hh, Lp), dtype=torch.float32, device="cuda")
-    U.ulysses_attn_fwd(r0["q"], r0["k"], r0["v"], o, lse, B, Lp, H, d, P, True)
+    U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o, lse, B, Lp, Lp, H, Hk, d, P, True)
     full_o = run.ohead["o"][0][:, :Lp]
     assert torch.equal(o.view(torch.int16), full_o.view(torch.int16)), "prefix rows differ from the full run"
     assert torch.equal(lse, run.lse[:, :, :Lp].contiguous())
     q, k, v = (run.oracle_head(n)[:, :Lp] for n in "qkv")
     if wl.backward:
         do = run.oracle_head("do")[:, :Lp]
-        dq, dk, dv = (torch.empty_like(o) for _ in range(3))
-        ws = torch.empty(U.ulysses_attn_bwd_workspace_bytes(B, Lp, H, d, P), dtype=torch.uint8, device="cuda")
-        U.ulysses_attn_bwd(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, ws, B, Lp, H, d, P, True)
+        dq = torch.empty_like(o)
+        dk, dv = torch.empty_like(r0["k"]), torch.empty_like(r0["v"])
+        ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, Lp, Lp, H, Hk, d, P), dtype=torch.uint8,
+                         device="cuda")
+        U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, ws, B, Lp, Lp, H, Hk, d, P,
+                               True)
         # dQ rows depend only on earlier keys: equal to the full run's
         assert torch.equal(dq.view(torch.int16), run.ohead["dq"][0][:, :Lp].view(torch.int16))
-        dq_r, dk_r, dv_r, o_r, lse_r, _ = oracle.attn_bwd(q, k, v, do, True)
+        dq_r, dk_r, dv_r = oracle.attn_bwd_gqa(q, k, v, do, True)
+        o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
         check_close("dQ prefix", to_f64(dq, "bf16"), dq_r, "bf16")
-        check_close("dK prefix problem", to_f64(dk, "bf16"), dk_r, "bf16")
-        check_close("dV prefix problem", to_f64(dv, "bf16"), dv_r, "bf16")
+        G = run.G
+        if G == 1:
+            allowed = {"dK": None, "dV": None}
+        else:   # a shared K/V head sums its G query heads' gradients
+            parts = {"dK": np.zeros((G,) + dk_r.shape), "dV": np.zeros((G,) + dv_r.shape)}
+            for h in range(Hh):
+                r = oracle.attn_bwd_head(q[0, :, h], k[0, :, h // G], v[0, :, h // G], do[0, :, h], True)
+                parts["dK"][h % G, 0, :, h // G] = r[1]
+                parts["dV"][h % G, 0, :, h // G] = r[2]
+            allowed = {nm: shared_head_allowed(parts[nm], want, "bf16") for nm, want in (("dK", dk_r), ("dV", dv_r))}
+        check_close("dK prefix problem", to_f64(dk, "bf16"), dk_r, "bf16", allowed=allowed["dK"])
+        check_close("dV prefix problem", to_f64(dv, "bf16"), dv_r, "bf16", allowed=allowed["dV"])
     else:
-        o_r, lse_r = oracle.attn_fwd(q, k, v, True)
+        o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
     check_close("O prefix", to_f64(o, "bf16"), o_r, "bf16")
     assert np.max(np.abs(lse.cpu().numpy() - lse_r)) <= 1e-3
 
@@ -198,16 +260,31 @@ def test_backward_sampled_rows_and_columns(key):
     q, k, v, do = (run.oracle_head(n) for n in ("q", "k", "v", "do"))
     dq, dk, dv = (to_f64(run.ohead[n][0], "bf16") for n in ("dq", "dk", "dv"))
     rng = np.random.default_rng(77)
-    cols = sorted({L - 1, L - 2, L - 63, L - 64, L - 65, L - 128, L - 129, L - 200, L - 256}
-                  | set(int(c) for c in rng.integers(L - 384, L, size=4)))
+    Lk, G = wl.Lk, run.G
+    cols = sorted({Lk - 1, Lk - 2, Lk - 63, Lk - 64, Lk - 65, Lk - 128, Lk - 129, Lk - 200, Lk - 256}
+                  | set(int(c) for c in rng.integers(Lk - 384, Lk, size=4)))
     for h in range(wl.Hp):
+        j = h // G
         for kind, rows in (("edge", edge_rows(wl, h)), ("uniform", uniform_rows(wl, h))):
-            ref = oracle.attn_rows(q[0, :, h], k[0, :, h], v[0, :, h], rows, wl.causal, do=do[0, :, h])
+            ref = oracle.attn_rows(q[0, :, h], k[0, :, j], v[0, :, j], rows, wl.causal, do=do[0, :, h])
             check_close(f"dQ {kind} rows head {h}", dq[0, rows, h], ref["dq"], "bf16", fro=(kind == "uniform"))
-        c, dk_r, dv_r = oracle.attn_dkv_cols(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h], cols, wl.causal,
-                                             row_block=64)
-        check_close(f"dK cols head {h}", dk[0, c, h], dk_r, "bf16")
-        check_close(f"dV cols head {h}", dv[0, c, h], dv_r, "bf16")
+    # bidirectional attention: every query row sees every column, so a column
+    # costs a full pass over the rows; check the first K/V head there
+    kv_heads = range(wl.Hkp) if wl.causal else range(1)
+    for j in kv_heads:
+        parts_k, parts_v = [], []
+        for h in range(j * G, (j + 1) * G):
+            c, dk_r, dv_r = oracle.attn_dkv_cols(q[0, :, h], k[0, :, j], v[0, :, j], do[0, :, h], cols, wl.causal,
+                                                 row_block=64)
+            parts_k.append(dk_r)
+            parts_v.append(dv_r)
+        if G == 1:
+            check_close(f"dK cols K/V head {j}", dk[0, c, j], parts_k[0], "bf16")
+            check_close(f"dV cols K/V head {j}", dv[0, c, j], parts_v[0], "bf16")
+        else:
+            wk, wv = np.sum(parts_k, axis=0), np.sum(parts_v, axis=0)
+            check_close(f"dK cols K/V head {j}", dk[0, c, j], wk, "bf16", allowed=shared_head_allowed(parts_k, wk, "bf16"))
+            check_close(f"dV cols K/V head {j}", dv[0, c, j], wv, "bf16", allowed=shared_head_allowed(parts_v, wv, "bf16"))
 
 
 @pytest.mark.parametrize("key", [n for n in NAMES if WORKLOADS[n].backward])
@@ -216,15 +293,18 @@ def test_backward_identities_over_full_outputs(key):
     wl = run.wl
     do = run.oracle_head("do")
     dk, dv = (to_f64(run.ohead[n][0], "bf16") for n in ("dk", "dv"))
-    # Rows of P sum to one, so sum_j dV_j = sum_i dO_i; rows of dS sum to zero, so
-    # sum_j dK_j = 0. These are gross-error checks over every output row (a wrong
-    # sign, scale or a large missing part); the bounds allow for bf16 rounding of
-    # P, dS and the outputs (2^-9 relative each) accumulated with any sign.
-    for h in range(wl.Hp):
-        sv = dv[0, :, h].sum(axis=0)
-        want = do[0, :, h].sum(axis=0)
-        bound_v = 2.0 ** -7 * (np.abs(dv[0, :, h]).sum(axis=0) + np.abs(do[0, :, h]).sum(axis=0))
-        assert np.all(np.abs(sv - want) <= bound_v), (h, np.max(np.abs(sv - want) / bound_v))
-        sk = dk[0, :, h].sum(axis=0)
-        bound_k = 2.0 ** -6 * np.abs(dk[0, :, h]).sum(axis=0) + 1e-6
-        assert np.all(np.abs(sk) <= bound_k), (h, np.max(np.abs(sk) / bound_k))
+    G = run.G
+    # Rows of P sum to one, so sum_j dV_j = sum_i dO_i (summed over the query
+    # heads that share the K/V head); rows of dS sum to zero, so sum_j dK_j = 0.
+    # These are gross-error checks over every output row (a wrong sign, scale
+    # or a large missing part); the bounds allow for bf16 rounding of P, dS and
+    # the outputs (2^-9 relative each) accumulated with any sign.
+    for j in range(wl.Hkp):
+        sv = dv[0, :, j].sum(axis=0)
+        dog = do[0, :, j * G:(j + 1) * G]
+        want = dog.sum(axis=(0, 1))
+        bound_v = 2.0 ** -7 * (np.abs(dv[0, :, j]).sum(axis=0) + np.abs(dog).sum(axis=(0, 1)))
+        assert np.all(np.abs(sv - want) <= bound_v), (j, np.max(np.abs(sv - want) / bound_v))
+        sk = dk[0, :, j].sum(axis=0)
+        bound_k = 2.0 ** -6 * np.abs(dk[0, :, j]).sum(axis=0) + 1e-6
+        assert np.all(np.abs(sk) <= bound_k), (j, np.max(np.abs(sk) / bound_k))

@@ -379,6 +379,22 @@ def test_sampled_rows_and_columns(causal):
     np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
 
 
+@pytest.mark.parametrize("Lq,Lk", [(70, 150), (150, 33)])
+def test_sampled_rows_and_columns_cross_attention(Lq, Lk):
+    # the sampled forms with queries and keys of different lengths (bidirectional)
+    d = 16
+    q, do = _rand((Lq, d), 60), _rand((Lq, d), 61)
+    k, v = _rand((Lk, d), 62), _rand((Lk, d), 63)
+    dq, dk, dv, o, lse, D = oracle.attn_bwd_head(q, k, v, do, False, row_block=32)
+    rows = [0, 1, Lq // 2, Lq - 1]
+    r = oracle.attn_rows(q, k, v, rows, False, do=do)
+    np.testing.assert_allclose(r["o"], o[rows], atol=1e-13)
+    np.testing.assert_allclose(r["dq"], dq[rows], atol=1e-12)
+    cols, dkc, dvc = oracle.attn_dkv_cols(q, k, v, do, [0, Lk - 1, Lk // 3], False, row_block=32)
+    np.testing.assert_allclose(dkc, dk[cols], atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # the seeded inputs
 # ---------------------------------------------------------------------------

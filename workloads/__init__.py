@@ -54,7 +54,22 @@ class Workload:
     v_scale: float = 0.5
     stress_rows: bool = False  # one seeded token row per head of Q and of K scaled by 8
     attn_all_ranks: bool = False  # True: attention on every virtual rank's head group
+    Lkv: int = 0        # key/value tokens when they differ from L (cross-attention); 0 = L
+    Hkv: int = 0        # key/value heads when fewer than H (grouped-query attention); 0 = H
     doc: str = ""
+
+    @property
+    def Lk(self) -> int:
+        return self.Lkv or self.L
+
+    @property
+    def Hk(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def Hkp(self) -> int:
+        """K/V heads a rank holds after the layout change (1 when replicated)."""
+        return self.Hk // self.P if self.Hk % self.P == 0 else 1
 
     @property
     def Hp(self) -> int:
@@ -71,6 +86,14 @@ class Workload:
     @property
     def head_shape(self) -> Tuple[int, ...]:
         return (self.P, self.B, self.L, self.Hp, self.d)
+
+    def shape_of(self, name: str) -> Tuple[int, ...]:
+        """Seq-layout shape of a drawn tensor (head layout for filler)."""
+        kv = name in ("k", "v", "fill_dk", "fill_dv")
+        L, H = (self.Lk, self.Hk) if kv else (self.L, self.H)
+        if name.startswith("fill_"):
+            return (self.P, self.B, L, self.Hkp if kv else self.Hp, self.d)
+        return (self.P, self.B, L // self.P, H, self.d)
 
     @property
     def elem_bytes(self) -> int:
@@ -95,6 +118,14 @@ WORKLOADS = {
                  doc="GPT 30B shape, 262,144 tokens, 4 local heads, stress rows, fwd+bwd"),
         Workload("L1m", 4, B=1, L=1048576, H=32, d=128, P=32, dtype="bf16",
                  backward=True, doc="1,048,576 tokens, 1 local head, fwd+bwd"),
+        Workload("gqa8-L131k", 5, B=1, L=131072, H=32, Hkv=8, d=128, P=8, dtype="bf16",
+                 backward=True, doc="grouped-query attention with 8 K/V heads (LLaMA-3-8B shape) at "
+                                    "the largest pure Ulysses degree P = 8: 4 query heads share 1 K/V head"),
+        Workload("gqa2-L131k", 6, B=1, L=131072, H=32, Hkv=2, d=128, P=8, dtype="bf16",
+                 backward=True, doc="2 K/V heads over P = 8: each K/V head replicated on 4 ranks"),
+        Workload("cross-L16k-L131k", 7, B=1, L=16384, Lkv=131072, H=32, d=128, P=8, dtype="bf16",
+                 backward=True, causal=False,
+                 doc="cross-attention: 16,384 queries over 131,072 keys, bidirectional, 4 local heads"),
     ]
 }
 
@@ -102,11 +133,11 @@ HEADLINE = "gpt7b-L131k"
 
 
 def custom(B, L, H, d, P, dtype="bf16", causal=True, backward=True, index=100,
-           qk_scale=0.5, v_scale=0.5, v_dist="normal", stress_rows=False) -> Workload:
+           qk_scale=0.5, v_scale=0.5, v_dist="normal", stress_rows=False, Lkv=0, Hkv=0) -> Workload:
     """A workload outside the named table (parity sweeps, edge cases)."""
-    return Workload(f"custom-{B}x{L}x{H}x{d}x{P}-{dtype}", index, B=B, L=L, H=H, d=d, P=P,
+    return Workload(f"custom-{B}x{L}x{Lkv}x{H}x{Hkv}x{d}x{P}-{dtype}", index, B=B, L=L, H=H, d=d, P=P,
                     dtype=dtype, backward=backward, causal=causal, qk_scale=qk_scale,
-                    v_scale=v_scale, v_dist=v_dist, stress_rows=stress_rows)
+                    v_scale=v_scale, v_dist=v_dist, stress_rows=stress_rows, Lkv=Lkv, Hkv=Hkv)
 
 
 # ---------------------------------------------------------------------------
@@ -135,7 +166,8 @@ def stress_positions(wl: Workload, name: str) -> Optional[np.ndarray]:
     if not wl.stress_rows or name not in ("q", "k"):
         return None
     rng = np.random.Generator(np.random.PCG64(_seed_seq(wl, "stress", TENSOR_IDS[name])))
-    return rng.integers(0, wl.L, size=(wl.B, wl.H), dtype=np.int64)
+    P, B, Lp, H, _ = wl.shape_of(name)
+    return rng.integers(0, P * Lp, size=(B, H), dtype=np.int64)
 
 
 def _dist(wl: Workload, name: str) -> Tuple[str, float]:
@@ -153,7 +185,7 @@ def host_tensor(wl: Workload, name: str) -> np.ndarray:
     Filler tensors (``fill_*``) have the head layout's element count and are
     returned in head layout ``[P, B, L, H/P, d]``.
     """
-    shape = wl.head_shape if name.startswith("fill_") else wl.seq_shape
+    shape = wl.shape_of(name)
     dist, scale = _dist(wl, name)
     out_f32 = np.empty(shape, dtype=np.float32)
     # one spawned child per leading (rank) slice, so the draw is chunkable
@@ -166,10 +198,11 @@ def host_tensor(wl: Workload, name: str) -> np.ndarray:
             out_f32[p] = rng.uniform(-1.0, 1.0, size=sub).astype(np.float32)
     pos = stress_positions(wl, name)
     if pos is not None:
-        for b in range(wl.B):
-            for h in range(wl.H):
+        Lp = shape[2]
+        for b in range(pos.shape[0]):
+            for h in range(pos.shape[1]):
                 t = int(pos[b, h])
-                out_f32[t // wl.Lp, b, t % wl.Lp, h, :] *= np.float32(8.0)
+                out_f32[t // Lp, b, t % Lp, h, :] *= np.float32(8.0)
     if wl.dtype == "fp32":
         return out_f32
     return f32_to_bf16_bits(out_f32)
@@ -183,7 +216,7 @@ def device_tensor(wl: Workload, name: str, device="cuda"):
     tensor of dtype bfloat16/float32 in seq layout (or head layout for filler).
     """
     import torch
-    shape = wl.head_shape if name.startswith("fill_") else wl.seq_shape
+    shape = wl.shape_of(name)
     dist, scale = _dist(wl, name)
     tdtype = torch.float32 if wl.dtype == "fp32" else torch.bfloat16
     out = torch.empty(shape, dtype=tdtype, device=device)
@@ -199,10 +232,11 @@ def device_tensor(wl: Workload, name: str, device="cuda"):
         del x
     pos = stress_positions(wl, name)
     if pos is not None:
-        for b in range(wl.B):
-            for h in range(wl.H):
+        Lp = shape[2]
+        for b in range(pos.shape[0]):
+            for h in range(pos.shape[1]):
                 t = int(pos[b, h])
-                row = out[t // wl.Lp, b, t % wl.Lp, h, :]
+                row = out[t // Lp, b, t % Lp, h, :]
                 # re-draw the stressed row in fp32 so the x8 is applied before rounding
                 seed = int(_seed_seq(wl, name, 1000 + b, h).generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
                 g.manual_seed(seed)
