@@ -41,6 +41,13 @@ What it computes (citations name a page and the passage on it):
   (the replication the "Head-count constraints" section mentions); the
   gradient map is the adjoint of that gather (replicas summed).
 
+* attn_fwd_block_sparse / attn_bwd_block_sparse -- attention restricted to the
+  (query block, key block) pairs a per-head block layout marks, plus the
+  causal mask inside them (paper-graph summary, section 3.4 and Figs 6-7 run
+  "blocked sparse attention" after the same all-to-all; the pages leave the
+  pattern open, so the layout is an input). A row that sees no key has zero
+  output, LSE -inf and zero gradients.
+
 * cross-attention -- attn_fwd_head / attn_bwd_head take keys of another length
   than the queries (papers.chlience.com note, section 5.4 lists cross-attention
   among the supported kinds); bidirectional only.
@@ -358,6 +365,129 @@ def head_to_seq_kv_grad(y: np.ndarray, B: int, L: int, Hkv: int, d: int, P: int)
     for p in range(P):
         for r in range(P):
             out[r, :, :, p // R] += y[p, :, r * Lp:(r + 1) * Lp, 0]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# block-sparse attention (paper-graph summary, section 3.4 and Figs 6-7: the
+# sparse pattern is applied locally after the all-to-all; pinyu.ai: each rank
+# holds the full sequence of its heads, so it can build the whole pattern)
+# ---------------------------------------------------------------------------
+
+def block_visible(layout_row: np.ndarray, block: int, i0: int, i1: int, L: int, causal: bool) -> np.ndarray:
+    """Token visibility of query rows i0..i1-1 (one block row or part of one)
+    under a block layout row: key j is visible to query i iff the layout marks
+    (i // block, j // block), and, when causal, j <= i."""
+    cols = np.arange(L)
+    vis = np.repeat(np.asarray(layout_row, dtype=bool), block)[:L][None, :].repeat(i1 - i0, axis=0)
+    if causal:
+        rows = np.arange(i0, i1)[:, None]
+        vis &= cols[None, :] <= rows
+    return vis
+
+
+def _masked_softmax_rows(s: np.ndarray, vis: np.ndarray):
+    """Softmax over the visible entries of each row; a row with no visible key
+    gets all-zero probabilities and LSE -inf."""
+    s = np.where(vis, s, -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    any_vis = np.isfinite(m)
+    m = np.where(any_vis, m, 0.0)
+    e = np.where(vis, np.exp(s - m), 0.0)
+    l = np.sum(e, axis=1, keepdims=True)
+    p = np.where(any_vis, e / np.where(any_vis, l, 1.0), 0.0)
+    lse = np.where(any_vis[:, 0], (m + np.log(np.where(any_vis, l, 1.0)))[:, 0], -np.inf)
+    return p, lse
+
+
+def attn_fwd_block_sparse_head(q, k, v, layout, block: int, causal: bool):
+    """One head: O and LSE of softmax(Q K^T / sqrt(d)) V restricted to the
+    visible (query, key) pairs of the block layout [nb, nb]."""
+    L, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    o = np.zeros((L, d))
+    lse = np.empty(L)
+    for bi, i0 in enumerate(range(0, L, block)):
+        i1 = min(L, i0 + block)
+        vis = block_visible(layout[bi], block, i0, i1, L, causal)
+        s = (q[i0:i1] @ k.T) * scale
+        p, lse[i0:i1] = _masked_softmax_rows(s, vis)
+        o[i0:i1] = p @ v
+    return o, lse
+
+
+def attn_bwd_block_sparse_head(q, k, v, do, layout, block: int, causal: bool):
+    """One head: exact gradient of the block-sparse attention above (the
+    masked entries are constants -inf, so dS = P o (dP - D) on the visible
+    pairs and 0 elsewhere). Returns (dq, dk, dv, o, lse, D)."""
+    L, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = np.zeros((L, d)), np.zeros((L, d)), np.zeros((L, d))
+    o, lse, D = np.zeros((L, d)), np.empty(L), np.empty(L)
+    for bi, i0 in enumerate(range(0, L, block)):
+        i1 = min(L, i0 + block)
+        vis = block_visible(layout[bi], block, i0, i1, L, causal)
+        s = (q[i0:i1] @ k.T) * scale
+        p, lse[i0:i1] = _masked_softmax_rows(s, vis)
+        ob = p @ v
+        o[i0:i1] = ob
+        Db = np.sum(do[i0:i1] * ob, axis=1)
+        D[i0:i1] = Db
+        dp = do[i0:i1] @ v.T
+        ds = p * (dp - Db[:, None])
+        dv += p.T @ do[i0:i1]
+        dq[i0:i1] = (ds @ k) * scale
+        dk += (ds.T @ q[i0:i1]) * scale
+    return dq, dk, dv, o, lse, D
+
+
+def attn_fwd_block_sparse(q, k, v, layout, block: int, causal: bool = True):
+    """q, k, v [B, L, H, d] (one rank's heads); layout [H, nb, nb] shared by the
+    batch. Returns O [B, L, H, d] and LSE [B, H, L]."""
+    B, L, H, d = q.shape
+    o = np.empty((B, L, H, d))
+    lse = np.empty((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            o[b, :, h], lse[b, h] = attn_fwd_block_sparse_head(q[b, :, h], k[b, :, h], v[b, :, h], layout[h],
+                                                               block, causal)
+    return o, lse
+
+
+def attn_bwd_block_sparse(q, k, v, do, layout, block: int, causal: bool = True):
+    """Gradients (dq, dk, dv) of attn_fwd_block_sparse."""
+    B, L, H, d = q.shape
+    dq, dk, dv = (np.empty((B, L, H, d)) for _ in range(3))
+    for b in range(B):
+        for h in range(H):
+            r = attn_bwd_block_sparse_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], layout[h], block, causal)
+            dq[b, :, h], dk[b, :, h], dv[b, :, h] = r[0], r[1], r[2]
+    return dq, dk, dv
+
+
+def attn_rows_block_sparse(q, k, v, rows, layout, block: int, causal: bool = True, do=None):
+    """Forward (and with dO the dQ row) of selected query rows of one head under a
+    block layout; each row costs O(L d). Returns dict o, lse (and D, dq)."""
+    L, d = k.shape
+    scale = 1.0 / math.sqrt(d)
+    rows = list(rows)
+    out = {"o": np.zeros((len(rows), d)), "lse": np.empty(len(rows))}
+    if do is not None:
+        out["D"] = np.empty(len(rows))
+        out["dq"] = np.zeros((len(rows), d))
+    for n, i in enumerate(rows):
+        vis = block_visible(layout[i // block], block, i, i + 1, L, causal)
+        s = (np.asarray(k, dtype=np.float64) @ np.asarray(q[i], dtype=np.float64)) * scale
+        p, lse = _masked_softmax_rows(s[None, :], vis)
+        out["lse"][n] = lse[0]
+        oi = p[0] @ np.asarray(v, dtype=np.float64)
+        out["o"][n] = oi
+        if do is not None:
+            doi = np.asarray(do[i], dtype=np.float64)
+            Di = float(doi @ oi)
+            dp = np.asarray(v, dtype=np.float64) @ doi
+            out["D"][n] = Di
+            out["dq"][n] = ((p[0] * (dp - Di)) @ np.asarray(k, dtype=np.float64)) * scale
     return out
 
 

@@ -540,3 +540,133 @@ def test_gqa_pipeline_equals_monolithic(Hq, Hkv, P):
     dqm, dkm, dvm = oracle.attn_bwd_gqa(glob(q), glob(k), glob(v), glob(do), True)
     for mine, ref in ((o, om), (dq, dqm), (dk, dkm), (dv, dvm)):
         np.testing.assert_allclose(glob(mine), ref, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# block-sparse attention
+# ---------------------------------------------------------------------------
+
+def _layout(nb, kind, seed=0):
+    if kind == "ones":
+        return np.ones((nb, nb), np.uint8)
+    if kind == "lower":
+        return np.tril(np.ones((nb, nb), np.uint8))
+    if kind == "diag":
+        return np.eye(nb, dtype=np.uint8)
+    rng = np.random.default_rng(seed)
+    lay = (rng.random((nb, nb)) < 0.4).astype(np.uint8)
+    np.fill_diagonal(lay, 1)
+    return lay
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_sparse_reduces_to_dense(causal):
+    L, d, block = 100, 8, 16
+    q, k, v, do = (_rand((L, d), s) for s in (70, 71, 72, 73))
+    nb = -(-L // block)
+    for kind in ("ones",) + (("lower",) if causal else ()):
+        o, lse = oracle.attn_fwd_block_sparse_head(q, k, v, _layout(nb, kind), block, causal)
+        od, lsed = oracle.attn_fwd_head(q, k, v, causal)
+        np.testing.assert_allclose(o, od, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, lsed, rtol=0, atol=1e-13)
+        g = oracle.attn_bwd_block_sparse_head(q, k, v, do, _layout(nb, kind), block, causal)
+        gd = oracle.attn_bwd_head(q, k, v, do, causal)
+        for a, b_ in zip(g[:3], gd[:3]):
+            np.testing.assert_allclose(a, b_, rtol=0, atol=1e-12)
+
+
+def test_block_diagonal_layout_is_independent_blocks():
+    # a diagonal layout cuts the sequence into independent causal blocks
+    L, d, block = 70, 6, 16
+    q, k, v, do = (_rand((L, d), s) for s in (74, 75, 76, 77))
+    nb = -(-L // block)
+    o, lse = oracle.attn_fwd_block_sparse_head(q, k, v, _layout(nb, "diag"), block, True)
+    g = oracle.attn_bwd_block_sparse_head(q, k, v, do, _layout(nb, "diag"), block, True)
+    for i0 in range(0, L, block):
+        sl = slice(i0, min(L, i0 + block))
+        ob, lseb = oracle.attn_fwd_head(q[sl], k[sl], v[sl], True)
+        np.testing.assert_allclose(o[sl], ob, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[sl], lseb, rtol=0, atol=1e-13)
+        gb = oracle.attn_bwd_head(q[sl], k[sl], v[sl], do[sl], True)
+        for a, b_ in zip(g[:3], gb[:3]):
+            np.testing.assert_allclose(a[sl], b_, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_sparse_matches_torch_masked_sdpa_and_autograd(causal):
+    torch = pytest.importorskip("torch")
+    L, d, block = 96, 16, 16
+    q, k, v, do = (_rand((L, d), s) for s in (78, 79, 80, 81))
+    nb = L // block
+    lay = _layout(nb, "random", seed=3)
+    o, lse = oracle.attn_fwd_block_sparse_head(q, k, v, lay, block, causal)
+    dq, dk, dv, *_ = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, causal)
+    vis = np.kron(lay, np.ones((block, block), np.uint8)).astype(bool)
+    if causal:
+        vis &= np.tril(np.ones((L, L), bool))
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None],
+                                                           attn_mask=torch.from_numpy(vis)[None])[0]
+    out.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=0, atol=1e-12)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=0, atol=1e-11)
+    s = (q @ k.T) / math.sqrt(d)
+    np.testing.assert_allclose(lse, np.log(np.sum(np.where(vis, np.exp(s), 0.0), axis=1)), rtol=0, atol=1e-12)
+
+
+def test_block_sparse_brute_force_and_sampled_rows():
+    L, d, block = 40, 5, 8
+    q, k, v, do = (_rand((L, d), s) for s in (82, 83, 84, 85))
+    nb = L // block
+    lay = _layout(nb, "random", seed=7)
+    o, lse = oracle.attn_fwd_block_sparse_head(q, k, v, lay, block, True)
+    for i in range(L):
+        js = [j for j in range(i + 1) if lay[i // block, j // block]]
+        w = [math.exp(sum(q[i, e] * k[j, e] for e in range(d)) / math.sqrt(d)) for j in js]
+        z = sum(w)
+        want = [sum(wj * v[j, e] for wj, j in zip(w, js)) / z for e in range(d)]
+        np.testing.assert_allclose(o[i], want, rtol=1e-12, atol=1e-13)
+        assert abs(lse[i] - math.log(z)) < 1e-12
+    dq, *_ = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, True)
+    rows = [0, 7, 8, 23, 39]
+    r = oracle.attn_rows_block_sparse(q, k, v, rows, lay, block, True, do=do)
+    np.testing.assert_allclose(r["o"], o[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], lse[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["dq"], dq[rows], rtol=0, atol=1e-12)
+
+
+def test_block_sparse_row_without_keys():
+    # a block row the layout leaves empty: zero output, LSE -inf, no gradient flow
+    L, d, block = 32, 4, 8
+    q, k, v, do = (_rand((L, d), s) for s in (86, 87, 88, 89))
+    lay = np.tril(np.ones((4, 4), np.uint8))
+    lay[2] = 0
+    o, lse = oracle.attn_fwd_block_sparse_head(q, k, v, lay, block, True)
+    assert np.all(o[16:24] == 0) and np.all(np.isneginf(lse[16:24]))
+    assert np.all(np.isfinite(lse[:16])) and np.all(np.isfinite(lse[24:]))
+    dq, dk, dv, *_ = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, True)
+    assert np.all(dq[16:24] == 0)
+    # dO of the empty rows does not reach dV
+    do2 = do.copy()
+    do2[16:24] = 123.0
+    _, _, dv2, *_ = oracle.attn_bwd_block_sparse_head(q, k, v, do2, lay, block, True)
+    np.testing.assert_allclose(dv2, dv, rtol=0, atol=1e-12)
+
+
+def test_block_layout_generator_structure():
+    from workloads import block_layout, custom
+    wl = custom(1, 1000, 4, 64, 2, block=64, window=3, n_global=1, n_random=2, index=321)
+    lay = block_layout(wl)
+    nb = 16
+    assert lay.shape == (4, nb, nb) and lay.dtype == np.uint8
+    for h in range(4):
+        assert np.all(np.triu(lay[h], 1) == 0)                   # causal: nothing above the diagonal
+        for i in range(nb):
+            row = lay[h, i]
+            assert all(row[j] for j in range(max(0, i - 2), i + 1))   # window of 3
+            assert row[0] == 1                                     # the global block
+            extra = row[:i + 1].sum() - len(set(range(max(0, i - 2), i + 1)) | {0})
+            assert extra == min(2, i + 1 - len(set(range(max(0, i - 2), i + 1)) | {0}))
+    assert not np.array_equal(lay[0], lay[1])                      # random blocks differ per head
+    np.testing.assert_array_equal(block_layout(wl), lay)          # seeded

@@ -34,7 +34,7 @@ ROOT_SEED = 230914509
 
 # tensor identities used in spawn keys (stable numbering; never reorder)
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "fill_o": 4, "fill_dq": 5,
-              "fill_dk": 6, "fill_dv": 7, "stress": 8}
+              "fill_dk": 6, "fill_dv": 7, "stress": 8, "layout": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -56,6 +56,10 @@ class Workload:
     attn_all_ranks: bool = False  # True: attention on every virtual rank's head group
     Lkv: int = 0        # key/value tokens when they differ from L (cross-attention); 0 = L
     Hkv: int = 0        # key/value heads when fewer than H (grouped-query attention); 0 = H
+    block: int = 0      # block-sparse attention: tokens per layout block (0 = dense)
+    window: int = 0     # ... each query block sees its `window` latest key blocks (itself included),
+    n_global: int = 0   # ... the first `n_global` key blocks,
+    n_random: int = 0   # ... and `n_random` further earlier blocks drawn per (head, block row)
     doc: str = ""
 
     @property
@@ -126,6 +130,10 @@ WORKLOADS = {
         Workload("cross-L16k-L131k", 7, B=1, L=16384, Lkv=131072, H=32, d=128, P=8, dtype="bf16",
                  backward=True, causal=False,
                  doc="cross-attention: 16,384 queries over 131,072 keys, bidirectional, 4 local heads"),
+        Workload("bsparse-L131k", 8, B=1, L=131072, H=32, d=128, P=8, dtype="bf16", backward=True,
+                 block=128, window=16, n_global=1, n_random=2,
+                 doc="blocked sparse causal attention, GPT 7B shape (Figs 6-7): 128-token blocks, a window of "
+                     "16 blocks, 1 global block and 2 random earlier blocks per block row and head"),
     ]
 }
 
@@ -133,11 +141,43 @@ HEADLINE = "gpt7b-L131k"
 
 
 def custom(B, L, H, d, P, dtype="bf16", causal=True, backward=True, index=100,
-           qk_scale=0.5, v_scale=0.5, v_dist="normal", stress_rows=False, Lkv=0, Hkv=0) -> Workload:
+           qk_scale=0.5, v_scale=0.5, v_dist="normal", stress_rows=False, Lkv=0, Hkv=0,
+           block=0, window=0, n_global=0, n_random=0) -> Workload:
     """A workload outside the named table (parity sweeps, edge cases)."""
     return Workload(f"custom-{B}x{L}x{Lkv}x{H}x{Hkv}x{d}x{P}-{dtype}", index, B=B, L=L, H=H, d=d, P=P,
                     dtype=dtype, backward=backward, causal=causal, qk_scale=qk_scale,
-                    v_scale=v_scale, v_dist=v_dist, stress_rows=stress_rows, Lkv=Lkv, Hkv=Hkv)
+                    v_scale=v_scale, v_dist=v_dist, stress_rows=stress_rows, Lkv=Lkv, Hkv=Hkv,
+                    block=block, window=window, n_global=n_global, n_random=n_random)
+
+
+def block_layout(wl: Workload, heads=None) -> np.ndarray:
+    """Block layout of a block-sparse workload: uint8 [H, nb, nb] over the global
+    heads (or the listed ones), nb = ceil(L / block); entry (h, i, j) = 1 when
+    query block i of head h attends key block j.
+
+    Row i holds its `window` latest blocks i-window+1 .. i, the first `n_global`
+    blocks, and `n_random` further blocks drawn without replacement from the
+    earlier ones (seeded per head). Bidirectional workloads mirror the window
+    (i-window+1 .. i+window-1) and draw random blocks from the whole row. The
+    structure -- not the arithmetic -- of the pages' "blocked sparse attention"
+    workload, whose pattern they leave open.
+    """
+    assert wl.block > 0
+    nb = -(-wl.L // wl.block)
+    heads = range(wl.H) if heads is None else heads
+    out = np.zeros((len(heads), nb, nb), dtype=np.uint8)
+    for n, h in enumerate(heads):
+        rng = np.random.Generator(np.random.PCG64(_seed_seq(wl, "layout", h)))
+        for i in range(nb):
+            lo = max(0, i - wl.window + 1)
+            hi = i + 1 if wl.causal else min(nb, i + wl.window)
+            out[n, i, lo:hi] = 1
+            out[n, i, :min(wl.n_global, nb)] = 1
+            pool = np.flatnonzero(out[n, i, :(i + 1 if wl.causal else nb)] == 0)
+            if wl.n_random and pool.size:
+                pick = rng.choice(pool, size=min(wl.n_random, pool.size), replace=False)
+                out[n, i, pick] = 1
+    return out
 
 
 # ---------------------------------------------------------------------------
