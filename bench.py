@@ -119,6 +119,19 @@ def npairs(L: int, causal: bool, Lk: int = 0) -> int:
     return L * (L + 1) // 2 if causal else L * (Lk or L)
 
 
+def npairs_layout(layout, block: int, L: int, causal: bool) -> int:
+    """Visible (query, key) pairs summed over the heads of a block layout [H][nb][nb]."""
+    import numpy as np
+    nb = layout.shape[1]
+    size = np.minimum(block, L - block * np.arange(nb))          # tokens per block
+    full = np.outer(size, size)
+    if causal:
+        w = np.tril(full, -1) + np.diag(size * (size + 1) // 2)
+    else:
+        w = full
+    return int(sum(int((w * (lay != 0)).sum()) for lay in layout))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +148,7 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(wl, seq_host, tokens: int):
+def cpu_baseline(wl, seq_host, tokens: int, layout=None):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
     import oracle
@@ -159,7 +172,15 @@ def cpu_baseline(wl, seq_host, tokens: int):
     t_perm = time.perf_counter() - t0
     f = {n: oracle.to_f64(heads[n][0, :(Lks if n in ("k", "v") else Ls), 0], wl.dtype) for n in heads}
     t0 = time.perf_counter()
-    if wl.backward:
+    if layout is not None:    # block-sparse: the layout of head 0 over the sampled prefix
+        nbs = -(-Ls // wl.block)
+        lay = layout[0, :nbs, :nbs]
+        if wl.backward:
+            oracle.attn_bwd_block_sparse_head(f["q"], f["k"], f["v"], f["do"], lay, wl.block, wl.causal)
+        else:
+            oracle.attn_fwd_block_sparse_head(f["q"], f["k"], f["v"], lay, wl.block, wl.causal)
+        flops = (14 if wl.backward else 4) * d * npairs_layout(lay[None], wl.block, Ls, wl.causal)
+    elif wl.backward:
         oracle.attn_bwd_head(f["q"], f["k"], f["v"], f["do"], wl.causal)
         flops = 14 * d * npairs(Ls, wl.causal, Lks)
     else:
@@ -188,7 +209,7 @@ def main():
     import torch
 
     import exact_attention_ulysses_amd as U
-    from workloads import HEADLINE, WORKLOADS, device_tensor
+    from workloads import HEADLINE, WORKLOADS, block_layout, device_tensor
 
     wl = WORKLOADS[args.workload or HEADLINE]
     B, L, H, d, P, Hh, causal = wl.B, wl.L, wl.H, wl.d, wl.P, wl.Hp, wl.causal
@@ -211,6 +232,9 @@ def main():
     lse = torch.empty((B, Hh, L), dtype=torch.float32, device=dev)
     ws = torch.empty(max(1, U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, causal)),
                      dtype=torch.uint8, device=dev)
+    # block-sparse workloads: rank 0's seeded block layout
+    layout_host = block_layout(wl, heads=range(Hh)) if wl.block else None
+    layout = torch.from_numpy(layout_host).to(dev) if wl.block else None
     r0 = {n: head[n][0] for n in ins}
     o0 = {n: ohead[n][0] for n in outs}
     stream = torch.cuda.current_stream()
@@ -223,9 +247,17 @@ def main():
                         tk * (1 + rep)))
         else:
             ops.append(("seq_to_head", lambda n=n: U.ulysses_seq_to_head(seq[n], head[n], B, L, H, d, P), 2 * tq))
-    ops.append(("attn_fwd", lambda: U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], lse, B, L, Lk, H,
-                                                           Hk, d, P, causal), 0))
-    if wl.backward:
+    if wl.block:
+        ops.append(("attn_fwd", lambda: U.ulysses_attn_fwd_block_sparse(r0["q"], r0["k"], r0["v"], o0["o"], lse,
+                                                                        layout, B, L, H, Hk, d, P, causal), 0))
+    else:
+        ops.append(("attn_fwd", lambda: U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], lse, B, L, Lk,
+                                                               H, Hk, d, P, causal), 0))
+    if wl.backward and wl.block:
+        ops.append(("attn_bwd", lambda: U.ulysses_attn_bwd_block_sparse(
+            r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], lse, o0["dq"], o0["dk"], o0["dv"], layout, ws, B, L, H, Hk,
+            d, P, causal), 0))
+    elif wl.backward:
         ops.append(("attn_bwd", lambda: U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], lse,
                                                                o0["dq"], o0["dk"], o0["dv"], ws, B, L, Lk, H, Hk,
                                                                d, P, causal), 0))
@@ -267,9 +299,11 @@ def main():
             per_op.setdefault(name, []).append(evs[s][i][0].elapsed_time(evs[s][i][1]))
     avg = {k: sum(v) / len(v) for k, v in per_op.items()}       # ms per launch of that op
 
-    npr = npairs(L, causal, Lk)
-    fwd_flops = 4 * d * npr * B * Hh
-    bwd_flops = 10 * d * npr * B * Hh
+    # visible (query, key) pairs over the rank's heads
+    npr_heads = (B * npairs_layout(layout_host, wl.block, L, causal) if wl.block
+                 else B * Hh * npairs(L, causal, Lk))
+    fwd_flops = 4 * d * npr_heads
+    bwd_flops = 10 * d * npr_heads
     attn_flops = fwd_flops + (bwd_flops if wl.backward else 0)
     perm_ms = sum(v for k, vs in per_op.items() if k in ("seq_to_head", "head_to_seq") for v in vs) / args.steps
     perm_bytes = sum(b for name, _, b in ops if name in ("seq_to_head", "head_to_seq"))
@@ -290,7 +324,7 @@ def main():
         "attn_fwd_ms": avg["attn_fwd"], "attn_fwd_TFLOPs": fwd_flops / (avg["attn_fwd"] * 1e-3) / 1e12,
         "attn_fwd_bwd_TFLOPs": attn_flops / (attn_ms * 1e-3) / 1e12,
         "attn_fwd_bwd_frac_peak": attn_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "attn_12dN_TFLOPs": (12 if wl.backward else 4) * d * npr * B * Hh / (attn_ms * 1e-3) / 1e12,
+        "attn_12dN_TFLOPs": (12 if wl.backward else 4) * d * npr_heads / (attn_ms * 1e-3) / 1e12,
         "seq_to_head_ms": avg["seq_to_head"], "head_to_seq_ms": avg["head_to_seq"],
         "transpose_GBps": perm_bytes / (perm_ms * 1e-3) / 1e9,
         "transpose_frac_peak": perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -310,11 +344,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         host = {n: seq[n].view(torch.int16).cpu().numpy().view("uint16") for n in ins}
-        cpu = cpu_baseline(wl, host, args.cpu_sample_tokens)
+        cpu = cpu_baseline(wl, host, args.cpu_sample_tokens, layout_host)
 
     metric = METRIC if wl.key == HEADLINE else METRIC.replace(
-        "causal attn", ("causal" if causal else "bidirectional") + (" grouped-query" if Hk != H else "")
-        + (" cross-" if Lk != L else " ") + "attn")
+        "causal attn", ("causal" if causal else "bidirectional") + (" block-sparse" if wl.block else "")
+        + (" grouped-query" if Hk != H else "") + (" cross-" if Lk != L else " ") + "attn")
     line = {
         "metric": metric, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -322,7 +356,9 @@ def main():
         "config": {"workload": wl.key, "B": B, "L": L, "H": H, "d_h": d, "P": P, "local_heads": Hh,
                    "causal": causal, "backward": wl.backward, "parallelism": "1 GPU, P virtual ranks",
                    **({"L_kv": Lk} if Lk != L else {}), **({"H_kv": Hk, "local_kv_heads": wl.Hkp}
-                                                          if Hk != H else {})},
+                                                          if Hk != H else {}),
+                   **({"block": wl.block, "window": wl.window, "global_blocks": wl.n_global,
+                       "random_blocks": wl.n_random, "visible_pairs": npr_heads} if wl.block else {})},
         "roofline": roofline, "cpu_baseline": cpu, "detail": detail,
     }
     print(json.dumps(line), flush=True)

@@ -31,6 +31,7 @@ STATUS_NAMES = {0: "ULYSSES_OK", 1: "ULYSSES_INVALID_ARGUMENT", 2: "ULYSSES_NOT_
 EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad",
            "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
            "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa", "ulysses_attn_bwd_gqa_workspace_bytes",
+           "ulysses_attn_fwd_block_sparse", "ulysses_attn_bwd_block_sparse",
            "ulysses_status_string", "ulysses_last_hip_error")
 
 
@@ -70,6 +71,11 @@ def lib() -> ctypes.CDLL:
     L.ulysses_attn_bwd_gqa.restype = ci
     L.ulysses_attn_bwd_gqa_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, ci]
     L.ulysses_attn_bwd_gqa_workspace_bytes.restype = sz
+    L.ulysses_attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.ulysses_attn_fwd_block_sparse.restype = ci
+    L.ulysses_attn_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz,
+                                                i64, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.ulysses_attn_bwd_block_sparse.restype = ci
     L.ulysses_status_string.argtypes = [ci]
     L.ulysses_status_string.restype = ctypes.c_char_p
     L.ulysses_last_hip_error.argtypes = []
@@ -207,6 +213,47 @@ def ulysses_attn_bwd_gqa(q, k, v, o, d_o, lse, dq, dk, dv, workspace, B: int, L_
     _check(st, "ulysses_attn_bwd_gqa")
 
 
+SPARSE_BLOCK = 128
+
+
+def _layout(layout, H_q: int, P: int, L: int, block: int) -> int:
+    torch = _torch()
+    if block <= 0:
+        raise ValueError("block must be positive")
+    nb = -(-L // block)
+    return _dev(layout, "layout", (H_q // P) * nb * nb, torch.uint8)
+
+
+def ulysses_attn_fwd_block_sparse(q, k, v, o, lse, layout, B: int, L: int, H_q: int, H_kv: int, d_h: int, P: int,
+                                  causal: bool = True, block: int = SPARSE_BLOCK, stream=None) -> None:
+    """Attention restricted to the blocks a uint8 layout [H_q/P][nb][nb] marks (bf16)."""
+    torch = _torch()
+    nq, nk, nl = _gqa_sizes("ulysses_attn_fwd_block_sparse", B, L, L, H_q, H_kv, d_h, P)
+    st = lib().ulysses_attn_fwd_block_sparse(
+        _dev(q, "q", nq), _dev(k, "k", nk, q.dtype), _dev(v, "v", nk, q.dtype), _dev(o, "o", nq, q.dtype),
+        _dev(lse, "lse", nl, torch.float32), _layout(layout, H_q, P, L, block), block, B, L, H_q, H_kv, d_h, P,
+        int(bool(causal)), dtype_code(q), _stream(stream))
+    _check(st, "ulysses_attn_fwd_block_sparse")
+
+
+def ulysses_attn_bwd_block_sparse(q, k, v, o, d_o, lse, dq, dk, dv, layout, workspace, B: int, L: int, H_q: int,
+                                  H_kv: int, d_h: int, P: int, causal: bool = True, block: int = SPARSE_BLOCK,
+                                  stream=None) -> None:
+    """dQ, dK, dV of ulysses_attn_fwd_block_sparse; workspace as for ulysses_attn_bwd_gqa (L_q = L_kv = L)."""
+    torch = _torch()
+    nq, nk, nl = _gqa_sizes("ulysses_attn_bwd_block_sparse", B, L, L, H_q, H_kv, d_h, P)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().ulysses_attn_bwd_block_sparse(
+        _dev(q, "q", nq), _dev(k, "k", nk, q.dtype), _dev(v, "v", nk, q.dtype), _dev(o, "o", nq, q.dtype),
+        _dev(d_o, "d_o", nq, q.dtype), _dev(lse, "lse", nl, torch.float32),
+        _dev(dq, "dq", nq, q.dtype), _dev(dk, "dk", nk, q.dtype), _dev(dv, "dv", nk, q.dtype),
+        _layout(layout, H_q, P, L, block), block, workspace.data_ptr(), wbytes, B, L, H_q, H_kv, d_h, P,
+        int(bool(causal)), dtype_code(q), _stream(stream))
+    _check(st, "ulysses_attn_bwd_block_sparse")
+
+
 def ulysses_attn_fwd(q, k, v, o, lse, B: int, L: int, H: int, d_h: int, P: int, causal: bool = True,
                      stream=None) -> None:
     """O = softmax(Q K^T / sqrt(d_h)) V on one rank's head block [B][L][H/P][d_h]; lse [B][H/P][L] fp32."""
@@ -249,4 +296,5 @@ def ulysses_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace, B: int, L: int
 __all__ = ["lib", "LIB_PATH", "BF16", "FP32", "UlyssesError", "EXPORTS", "kv_local_heads", "ulysses_seq_to_head",
            "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad", "ulysses_attn_fwd",
            "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa",
-           "ulysses_attn_bwd_gqa_workspace_bytes"]
+           "ulysses_attn_bwd_gqa_workspace_bytes", "ulysses_attn_fwd_block_sparse", "ulysses_attn_bwd_block_sparse",
+           "SPARSE_BLOCK"]

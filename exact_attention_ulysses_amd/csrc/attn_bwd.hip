@@ -29,6 +29,7 @@
 
 #include <type_traits>
 
+#include "block_sparse.h"
 #include "common.h"
 #include "kernels.h"
 #include "mfma_frag.h"
@@ -74,12 +75,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
 // shares a SIMD and the producer's exponentials and products run while the
 // consumer's MFMAs do. Tiles are double buffered; each step ends with two
 // barriers (hand-over, then the staging of the next tile).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
-    float scale) {
+    float scale, const uint8_t* __restrict__ layout, int nb) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256, RSTEP = 256 / CPR;
   constexpr int ST = Stride<D>::both;  // Q and dO tiles are read along rows and transposed
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
@@ -88,6 +89,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float dls[2][BQ];
   // hand-over: [buffer][producer][P or dS][half u * 2 + chunk c][lane]
   __shared__ __attribute__((aligned(16))) bf16x8 hand[2][4][2][4][64];
+  // block layouts: the active (query head g, query block i) pairs of this key
+  // block, g * 8192 + i, in visiting order
+  __shared__ uint16_t pairs[SPARSE ? kMaxSparsePairs : 1];
+  __shared__ int npairs;
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -108,9 +113,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
 
   const int qstart = CAUSAL ? kb * 128 : 0;
   const int nqt = (Lq - qstart + BQ - 1) / BQ;   // query tiles per query head
-  const int nsteps = G * nqt;
+  int nsteps = G * nqt;
   // under the causal mask only the first two query tiles reach above a key of this block
   const int nmask = CAUSAL ? min(nqt, 2) : 0;
+  if constexpr (SPARSE) {
+    // wave 0 lists the active query blocks of this key block's layout column for
+    // each query head of the group (causal: from the diagonal block on); each
+    // query block is two 64-row query tiles
+    if (wave == 0) {
+      int cnt = 0;
+      for (int g = 0; g < G; ++g) {
+        const uint8_t* col = layout + (size_t)(hk * G + g) * nb * nb + kb;
+        for (int base = CAUSAL ? kb : 0; base < nb; base += 64) {
+          const int i = base + lane;
+          const bool act = i < nb && col[(size_t)i * nb] != 0;
+          const uint64_t m = __ballot(act);
+          if (act) pairs[cnt + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = (uint16_t)(g * 8192 + i);
+          cnt += __builtin_popcountll(m);
+        }
+      }
+      if (lane == 0) npairs = cnt;
+    }
+    __syncthreads();
+    nsteps = 2 * npairs;
+  }
 
   // staging of Q, dO, lse, delta by the producer waves (threads 0..255) through
   // buffer loads; rows past the end of the sequence read as zero (the range
@@ -125,20 +151,41 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsq + scol) * 2);
   u32x4 qreg[CH], dreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
-  // step t handles query tile t mod nqt of the group's query head t div nqt
+  // Step t handles the query tile starting at row q0 of the group's query head
+  // g: dense, tile t mod nqt of head t div nqt; with a block layout, half t & 1
+  // of the listed pair t / 2. `diag` marks the tiles that reach above a key of
+  // this block under the causal mask.
   const FastDiv fq = make_fastdiv((uint32_t)nqt);
+  auto tile_of = [&](int t, int& g, int& q0, bool& diag) {
+    if constexpr (SPARSE) {
+      const int e = pairs[t >> 1];
+      g = e >> 13;
+      const int i = e & 8191;
+      q0 = (2 * i + (t & 1)) * BQ;
+      diag = CAUSAL && i == kb;
+    } else {
+      g = (int)fdiv((uint32_t)t, fq);
+      const int qt = t - g * nqt;
+      q0 = qstart + qt * BQ;
+      diag = CAUSAL && qt < nmask;
+    }
+  };
   auto load_tile = [&](int t) {
-    const int g = (int)fdiv((uint32_t)t, fq), qt = t - g * nqt;
-    const uint32_t soff = (uint32_t)(qstart + qt * BQ) * (uint32_t)(rsq * 2) + (uint32_t)(g * D * 2);
+    int g, q0;
+    bool diag;
+    tile_of(t, g, q0, diag);
+    const uint32_t soff = (uint32_t)q0 * (uint32_t)(rsq * 2) + (uint32_t)(g * D * 2);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       qreg[j] = buf_load16(qrs, voff[j] + soff, 0);
       dreg[j] = buf_load16(drs, voff[j] + soff, 0);
     }
     if (tid < BQ) {
-      const int qi = qstart + qt * BQ + tid;
-      // rows past the end get lse = +inf, so their probabilities are exactly 0
-      lse_r = qi < Lq ? lseh[(size_t)g * Lq + qi] * kLog2e : INFINITY;
+      const int qi = q0 + tid;
+      // rows past the end, and rows that see no key (LSE -inf, block layouts
+      // only), get lse = +inf, so their probabilities are exactly 0
+      const float l = qi < Lq ? lseh[(size_t)g * Lq + qi] : INFINITY;
+      lse_r = l == -INFINITY ? INFINITY : l * kLog2e;
       dl_r = qi < Lq ? dlh[(size_t)g * Lq + qi] : 0.f;
     }
   };
@@ -168,10 +215,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       }
     }
     // step s (LDS buffer s & 1) handles query tile qt of one query head
-    auto produce = [&](int s, int qt, auto mask_tag) {
+    auto produce = [&](int s, int q0, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int cur = s & 1;
-      const int q0 = qstart + qt * BQ;
       const __bf16* Qc = Qs[cur];
       const __bf16* Dc = Ds[cur];
       f32x16 sc[2], dp[2];
@@ -212,17 +258,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
         }
       }
     };
-    load_tile(0);
+    if (nsteps > 0) load_tile(0);
     store_tile(0);
     __syncthreads();
     if (nsteps > 1) load_tile(1);
     for (int s = 0; s <= nsteps; ++s) {
       if (s < nsteps) {
-        const int qt = s - (int)fdiv((uint32_t)s, fq) * nqt;
-        if (CAUSAL && qt < nmask)
-          produce(s, qt, std::integral_constant<bool, true>{});
+        int g, q0;
+        bool diag;
+        tile_of(s, g, q0, diag);
+        if (diag)
+          produce(s, q0, std::integral_constant<bool, true>{});
         else
-          produce(s, qt, std::integral_constant<bool, false>{});
+          produce(s, q0, std::integral_constant<bool, false>{});
       }
       __syncthreads();  // hand-over of tile s; consumers are done with tile s-1's buffers
       if (s + 1 < nsteps) store_tile((s + 1) & 1);
@@ -272,11 +320,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale) {
+    __bf16* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale,
+    const uint8_t* __restrict__ layout, int nb) {
   constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256, RSTEP = 256 / CPR;
   constexpr int KST = Stride<D>::both;  // K: rows for S^T = K Q^T, transposed for dQ^T += K^T dS^T
   constexpr int VST = Stride<D>::row;   // V: rows for dP^T = V dO^T
@@ -309,7 +358,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       df[ks] = bf16x8{};
     }
   }
-  const float nlse2 = valid ? -lse[(size_t)hb * Lq + qrow] * kLog2e : 0.f;
+  // a row that sees no key (LSE -inf, block layouts only) has probabilities 0
+  const float lse_i = valid ? lse[(size_t)hb * Lq + qrow] : 0.f;
+  const float nlse2 = lse_i == -INFINITY ? -INFINITY : -lse_i * kLog2e;
   const float dl = valid ? delta[(size_t)hb * Lq + qrow] : 0.f;
 
   f32x16 dqacc[DT];
@@ -343,9 +394,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     }
   };
 
-  auto tile = [&](int kb, auto edge_tag) {
+  // key tile kb in LDS buffer cur; then the staged tile goes to the other
+  // buffer (if store) and key tile next2 into the staging registers (if >= 0)
+  auto tile = [&](int cur, int kb, bool store, int next2, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const int cur = kb & 1;
     const __bf16* Kc = Ks[cur];
     const __bf16* Vc = Vs[cur];
     const int k0 = kb * BN;
@@ -378,20 +430,45 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
           dqacc[dt] = mfma32(frag_col<KST>(Kc, 32 * mt + 16 * c, 32 * dt, lane), dsf, dqacc[dt]);
       }
     }
-    if (kb + 1 < nkb) store_tile(cur ^ 1);
-    if (kb + 2 < nkb) load_tile(kb + 2);
+    if (store) store_tile(cur ^ 1);
+    if (next2 >= 0) load_tile(next2);
     __syncthreads();
   };
+  const auto steady = std::integral_constant<bool, false>{};
+  const auto edge = std::integral_constant<bool, true>{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  if (nkb > 1) load_tile(1);
-  // as in the forward pass: only the last two key tiles (causal) or a ragged last tile need a mask
-  const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
-  int kb = 0;
-  for (; kb < nsteady; ++kb) tile(kb, std::integral_constant<bool, false>{});
-  for (; kb < nkb; ++kb) tile(kb, std::integral_constant<bool, true>{});
+  if constexpr (!SPARSE) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    if (nkb > 1) load_tile(1);
+    // as in the forward pass: only the last two key tiles (causal) or a ragged last tile need a mask
+    const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
+    int kb = 0;
+    for (; kb < nsteady; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, steady);
+    for (; kb < nkb; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, edge);
+  } else {
+    // active key blocks of this query block, two key tiles each, as in the forward kernel
+    LayoutScan scan;
+    scan.reset(layout + ((size_t)h * nb + qb) * nb, 1, 0, CAUSAL ? qb + 1 : nb);
+    int j = scan.next(lane);
+    if (j >= 0) {
+      int jn = scan.next(lane);
+      load_tile(2 * j);
+      store_tile(0);
+      __syncthreads();
+      load_tile(2 * j + 1);
+      int half = 0;
+      while (j >= 0) {
+        tile(half, 2 * j + half, half == 0 || jn >= 0, jn >= 0 ? 2 * jn + half : -1, edge);
+        if (half == 1) {
+          j = jn;
+          if (j >= 0) jn = scan.next(lane);
+        }
+        half ^= 1;
+      }
+    }
+  }
 
   if (valid) {
     __bf16* row = dq + qoff + (size_t)qrow * rsq;
@@ -552,16 +629,27 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
   const float sl2 = scale * kLog2e;
   const int nkhb = s.B * s.Hk;
   const int nkb = (s.Lk + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                     (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale);
+  const int nb = (s.Lk + kSparseBlock - 1) / kSparseBlock;
+  if (s.layout)
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nhb = s.B * s.Hq;
   const int nqb = (s.Lq + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                     (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale);
+  if (s.layout)
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, s.layout, nb);
+  else
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@
 
 #include <type_traits>
 
+#include "block_sparse.h"
 #include "common.h"
 #include "kernels.h"
 #include "mfma_frag.h"
@@ -39,11 +40,11 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
-    float sl2) {
+    float sl2, const uint8_t* __restrict__ layout, int nb) {
   constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CH = BN * CPR / 256;         // chunks per thread per tile
@@ -115,11 +116,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     }
   };
 
-  // One key tile. EDGE tiles cross the diagonal (or the end of the sequence)
-  // and need the mask; the steady-state loop runs without it.
-  auto tile = [&](int kb, auto edge_tag) {
+  // One key tile kb, held in LDS buffer cur; afterwards the tile in the
+  // staging registers goes to the other buffer (if store) and key tile `next2`
+  // is loaded into the registers (if >= 0). EDGE tiles cross the diagonal (or
+  // the end of the keys) and need the mask; the steady-state loop runs without it.
+  auto tile = [&](int cur, int kb, bool store, int next2, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const int cur = kb & 1;
     const __bf16* Kc = Ks[cur];
     const __bf16* Vc = Vs[cur];
     const int k0 = kb * BN;
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
       m_run = m2;
     }
-    const float nm = -m_run;
+    // (a block-sparse row may meet a fully masked tile before any visible key)
+    const float nm = (SPARSE && m_run == -INFINITY) ? 0.f : -m_run;
     float rsum = 0.f;
     bf16x8 pf[4];
 #pragma unroll
@@ -179,24 +182,55 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<VST>(Vc, 16 * c, 32 * dt, lane), pf[c], oacc[dt]);
     }
 
-    if (kb + 1 < nkb) store_tile(cur ^ 1);
-    if (kb + 2 < nkb) load_tile(kb + 2);
+    if (store) store_tile(cur ^ 1);
+    if (next2 >= 0) load_tile(next2);
     __syncthreads();
   };
+  const auto steady = std::integral_constant<bool, false>{};
+  const auto edge = std::integral_constant<bool, true>{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  if (nkb > 1) load_tile(1);
-  // causal: only the last two key tiles reach above a query row of this block;
-  // otherwise only a ragged last tile holds keys past the end
-  const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
-  int kb = 0;
-  for (; kb < nsteady; ++kb) tile(kb, std::integral_constant<bool, false>{});
-  for (; kb < nkb; ++kb) tile(kb, std::integral_constant<bool, true>{});
+  if constexpr (!SPARSE) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    if (nkb > 1) load_tile(1);
+    // causal: only the last two key tiles reach above a query row of this block;
+    // otherwise only a ragged last tile holds keys past the end
+    const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
+    int kb = 0;
+    for (; kb < nsteady; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, steady);
+    for (; kb < nkb; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, edge);
+  } else {
+    // The active key blocks j of this query block (ascending; causal: j <= qb),
+    // two key tiles each: tile (j, half) sits in LDS buffer `half`. A second
+    // tile past the end of the keys is fully masked (its loads read zeros).
+    // Every tile takes the masked path, which masks only where a tile crosses
+    // the diagonal or the end of the keys.
+    LayoutScan scan;
+    scan.reset(layout + ((size_t)h * nb + qb) * nb, 1, 0, CAUSAL ? qb + 1 : nb);
+    int j = scan.next(lane);
+    if (j >= 0) {
+      int jn = scan.next(lane);
+      load_tile(2 * j);
+      store_tile(0);
+      __syncthreads();
+      load_tile(2 * j + 1);
+      int half = 0;
+      while (j >= 0) {
+        // next tile: (j, 1) or (jn, 0); the one after: (jn, half)
+        tile(half, 2 * j + half, half == 0 || jn >= 0, jn >= 0 ? 2 * jn + half : -1, edge);
+        if (half == 1) {
+          j = jn;
+          if (j >= 0) jn = scan.next(lane);
+        }
+        half ^= 1;
+      }
+    }
+  }
 
+  // a row that sees no key (possible only under a block layout) has zero output and LSE -inf
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < Lq) {
     __bf16* orow = o + qoff + (size_t)qrow * rsq;
 #pragma unroll
@@ -205,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
     }
-    if (hl == 0) lse[(size_t)hb * Lq + qrow] = (m_run + log2f(l_tot)) * kLn2;
+    if (hl == 0) lse[(size_t)hb * Lq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -277,9 +311,15 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   const int nqb = (s.Lq + 127) / 128;
   const int nhb = s.B * s.Hq;
   const float sl2 = kLog2e / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq, s.Hk,
-                     s.Hq / s.Hk, nqb, nhb, sl2);
+  const int nb = (s.Lk + kSparseBlock - 1) / kSparseBlock;
+  if (s.layout)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
+                       s.Hk, s.Hq / s.Hk, nqb, nhb, sl2, s.layout, nb);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
+                       s.Hk, s.Hq / s.Hk, nqb, nhb, sl2, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ struct AttnShape {
                 // key head h / (Hq / Hk)
   int D;        // head dim (64 or 128)
   bool causal;
+  // block-sparse attention (bf16 only): per local query head uint8 layout
+  // [Hq][nb][nb] over 128-token blocks, nb = ceil(L / 128); nullptr = dense
+  const uint8_t* layout = nullptr;
 };
 
 // bf16 operands, fp32 lse

@@ -4,6 +4,7 @@
 
 
 #include "../../include/ulysses.h"
+#include "block_sparse.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -147,18 +148,40 @@ int64_t q_bytes(const AttnShape& s, int dtype) { return (int64_t)s.B * s.Lq * s.
 int64_t k_bytes(const AttnShape& s, int dtype) { return (int64_t)s.B * s.Lk * s.Hk * s.D * elem_size(dtype); }
 int64_t lse_bytes(const AttnShape& s) { return (int64_t)s.B * s.Hq * s.Lq * 4; }
 
+// Block layouts: 128-token blocks, bf16, self-attention; the dK/dV kernel's
+// pair list bounds the query heads per K/V head and the blocks per column.
+int sparse_dims(const uint8_t* layout, int64_t block, int64_t Lq, int64_t Lk, int dtype, AttnShape* s,
+                bool backward) {
+  if (!layout) return ULYSSES_INVALID_ARGUMENT;
+  if (block != kSparseBlock || dtype != ULYSSES_BF16 || Lq != Lk) return ULYSSES_UNSUPPORTED;
+  const int64_t nb = (Lk + kSparseBlock - 1) / kSparseBlock, G = s->Hq / s->Hk;
+  if (backward && (G > kMaxSparseGroup || G * nb > kMaxSparsePairs)) return ULYSSES_UNSUPPORTED;
+  s->layout = layout;
+  return ULYSSES_OK;
+}
+
+int64_t layout_bytes(const AttnShape& s) {
+  const int64_t nb = (s.Lk + kSparseBlock - 1) / kSparseBlock;
+  return (int64_t)s.Hq * nb * nb;
+}
+
 int attn_fwd_entry(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Lq,
                    int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal, int dtype,
-                   void* stream) {
+                   void* stream, const uint8_t* layout = nullptr, int64_t block = 0) {
   if (!q || !k || !v || !o || !lse) return ULYSSES_INVALID_ARGUMENT;
   AttnShape s;
   int st = attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s);
   if (st != ULYSSES_OK) return st;
+  if (block != 0 || layout) {
+    st = sparse_dims(layout, block, Lq, Lk, dtype, &s, false);
+    if (st != ULYSSES_OK) return st;
+  }
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return ULYSSES_MISALIGNED;
   const int64_t tq = q_bytes(s, dtype), tk = k_bytes(s, dtype);
   const Range ro = range_of(o, tq), rl = range_of(lse, lse_bytes(s));
-  const Range rin[3] = {range_of(q, tq), range_of(k, tk), range_of(v, tk)};
+  const Range rin[4] = {range_of(q, tq), range_of(k, tk), range_of(v, tk),
+                        range_of(layout, layout ? layout_bytes(s) : 0)};
   for (const Range& r : rin)
     if (overlap(ro, r) || overlap(rl, r)) return ULYSSES_ALIASING;
   if (overlap(ro, rl)) return ULYSSES_ALIASING;
@@ -177,11 +200,15 @@ size_t attn_ws_entry(int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv,
 int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
                    void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Lq,
                    int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal, int dtype,
-                   void* stream) {
+                   void* stream, const uint8_t* layout = nullptr, int64_t block = 0) {
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv || !workspace) return ULYSSES_INVALID_ARGUMENT;
   AttnShape s;
   int st = attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s);
   if (st != ULYSSES_OK) return st;
+  if (block != 0 || layout) {
+    st = sparse_dims(layout, block, Lq, Lk, dtype, &s, true);
+    if (st != ULYSSES_OK) return st;
+  }
   const void* al16[] = {q, k, v, o, d_o, dq, dk, dv, workspace};
   for (const void* p : al16)
     if (!aligned(p, 16)) return ULYSSES_MISALIGNED;
@@ -190,8 +217,8 @@ int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, c
   if (workspace_bytes < need) return ULYSSES_WORKSPACE_TOO_SMALL;
   const int64_t tq = q_bytes(s, dtype), tk = k_bytes(s, dtype);
   const Range outs[4] = {range_of(dq, tq), range_of(dk, tk), range_of(dv, tk), range_of(workspace, (int64_t)need)};
-  const Range ins[6] = {range_of(q, tq), range_of(k, tk), range_of(v, tk), range_of(o, tq), range_of(d_o, tq),
-                        range_of(lse, lse_bytes(s))};
+  const Range ins[7] = {range_of(q, tq), range_of(k, tk), range_of(v, tk), range_of(o, tq), range_of(d_o, tq),
+                        range_of(lse, lse_bytes(s)), range_of(layout, layout ? layout_bytes(s) : 0)};
   for (int i = 0; i < 4; ++i) {
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return ULYSSES_ALIASING;
@@ -272,6 +299,23 @@ int ulysses_attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                          int causal, int dtype, void* stream) {
   return attn_bwd_entry(q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, L_q, L_kv, H_q, H_kv, d_h,
                         P, causal, dtype, stream);
+}
+
+int ulysses_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const uint8_t* layout, int64_t block, int64_t B, int64_t L, int64_t H_q,
+                                  int64_t H_kv, int64_t d_h, int64_t P, int causal, int dtype, void* stream) {
+  if (!layout) return ULYSSES_INVALID_ARGUMENT;
+  return attn_fwd_entry(q, k, v, o, lse, B, L, L, H_q, H_kv, d_h, P, causal, dtype, stream, layout, block);
+}
+
+int ulysses_attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                                  const float* lse, void* dq, void* dk, void* dv, const uint8_t* layout,
+                                  int64_t block, void* workspace, size_t workspace_bytes, int64_t B, int64_t L,
+                                  int64_t H_q, int64_t H_kv, int64_t d_h, int64_t P, int causal, int dtype,
+                                  void* stream) {
+  if (!layout) return ULYSSES_INVALID_ARGUMENT;
+  return attn_bwd_entry(q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, L, L, H_q, H_kv, d_h, P,
+                        causal, dtype, stream, layout, block);
 }
 
 const char* ulysses_status_string(int status) {

@@ -199,6 +199,38 @@ size_t ulysses_attn_bwd_gqa_workspace_bytes(int64_t B, int64_t L_q, int64_t L_kv
                                             int64_t H_kv, int64_t d_h, int64_t P, int causal,
                                             int dtype);
 
+/*
+ * Block-sparse attention: ulysses_attn_fwd_gqa / ulysses_attn_bwd_gqa (self-
+ * attention, L_q = L_kv = L) restricted to the (query block, key block) pairs a
+ * block layout marks. The pages run "blocked sparse attention" after the same
+ * all-to-all and note that each rank, holding the full sequence of its heads,
+ * applies the sparsity pattern locally (paper-graph summary, section 3.4 and
+ * Figs 6-7); they do not fix the pattern, so the layout is an argument.
+ *   layout  device uint8 [H_q/P][nb][nb], nb = ceil(L / block), row-major, one
+ *           per local query head and shared by the batch: entry (h, i, j) != 0
+ *           lets the queries of block i attend the keys of block j. Read only.
+ *   block   tokens per layout block; 128 is the only supported value.
+ * Key j is visible to query i iff layout[h][i / block][j / block] != 0 and,
+ * with causal = 1, j <= i (entries above the block diagonal are then ignored).
+ * A query row that sees no key gets O = 0 and lse = -inf, and passes no
+ * gradient. bf16 only (ULYSSES_UNSUPPORTED otherwise). The backward pass also
+ * needs (H_q/H_kv) <= 8 and (H_q/H_kv) * nb <= 8192 (UNSUPPORTED otherwise);
+ * its workspace is ulysses_attn_bwd_gqa_workspace_bytes(B, L, L, ...).
+ * Only the active blocks are computed.
+ */
+int ulysses_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  const uint8_t* layout, int64_t block,
+                                  int64_t B, int64_t L, int64_t H_q, int64_t H_kv, int64_t d_h, int64_t P,
+                                  int causal, int dtype, void* stream);
+
+int ulysses_attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                                  const void* d_o, const float* lse,
+                                  void* dq, void* dk, void* dv,
+                                  const uint8_t* layout, int64_t block,
+                                  void* workspace, size_t workspace_bytes,
+                                  int64_t B, int64_t L, int64_t H_q, int64_t H_kv, int64_t d_h, int64_t P,
+                                  int causal, int dtype, void* stream);
+
 /* Static, NUL-terminated name of a status code ("ULYSSES_OK", ...). */
 const char* ulysses_status_string(int status);
 

@@ -491,6 +491,34 @@ def attn_rows_block_sparse(q, k, v, rows, layout, block: int, causal: bool = Tru
     return out
 
 
+def attn_dkv_cols_block_sparse(q, k, v, do, cols, layout, block: int, causal: bool = True):
+    """dK and dV of selected key columns of one head under a block layout: only
+    the block rows whose layout row reaches a selected column's block are
+    formed (each in full, for its LSE and D). Returns (cols, dk, dv)."""
+    L, d = k.shape
+    scale = 1.0 / math.sqrt(d)
+    cols = np.asarray(sorted(set(int(c) for c in cols)), dtype=np.int64)
+    cblocks = np.unique(cols // block)
+    dk = np.zeros((len(cols), d))
+    dv = np.zeros((len(cols), d))
+    kk = np.asarray(k, dtype=np.float64)
+    vv = np.asarray(v, dtype=np.float64)
+    for bi, i0 in enumerate(range(0, L, block)):
+        i1 = min(L, i0 + block)
+        if not np.any(np.asarray(layout[bi])[cblocks]) or (causal and i1 - 1 < cols.min()):
+            continue
+        qb = np.asarray(q[i0:i1], dtype=np.float64)
+        dob = np.asarray(do[i0:i1], dtype=np.float64)
+        vis = block_visible(layout[bi], block, i0, i1, L, causal)
+        p, _ = _masked_softmax_rows((qb @ kk.T) * scale, vis)
+        Db = np.sum(dob * (p @ vv), axis=1)
+        pc = p[:, cols]
+        dsc = pc * (dob @ vv[cols].T - Db[:, None])
+        dk += (dsc.T @ qb) * scale
+        dv += pc.T @ dob
+    return cols, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # sampled evaluation for sizes where the full quadratic oracle is too slow
 # ---------------------------------------------------------------------------

@@ -215,3 +215,41 @@ def test_gqa_workspace_and_reductions():
         lib.ulysses_attn_bwd_workspace_bytes(1, 4096, 16, 128, 4, 1, U.BF16)
     assert U.kv_local_heads(8, 8) == 1 and U.kv_local_heads(16, 8) == 2
     assert U.kv_local_heads(2, 8) == 1 and U.kv_local_heads(3, 8) == 0
+
+
+def fwd_bs(layout=A + 6 * GB, block=128, B=1, L=1024, Hq=32, Hkv=8, d=128, P=8, causal=1, dtype=U.BF16, **ptrs):
+    p = dict(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB)
+    p.update(ptrs)
+    return U.lib().ulysses_attn_fwd_block_sparse(p["q"], p["k"], p["v"], p["o"], p["lse"], layout, block, B, L, Hq,
+                                                 Hkv, d, P, causal, dtype, None)
+
+
+def bwd_bs(layout=A + 12 * GB, block=128, ws_bytes=None, B=1, L=1024, Hq=32, Hkv=8, d=128, P=8, causal=1,
+           dtype=U.BF16, **ptrs):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"]
+    p = {n: A + i * GB for i, n in enumerate(names)}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = U.lib().ulysses_attn_bwd_gqa_workspace_bytes(B, L, L, Hq, Hkv, d, P, causal, dtype)
+    return U.lib().ulysses_attn_bwd_block_sparse(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"],
+                                                 p["dv"], layout, block, p["ws"], ws_bytes, B, L, Hq, Hkv, d, P,
+                                                 causal, dtype, None)
+
+
+def test_block_sparse_validation():
+    assert fwd_bs(layout=None) == 1
+    assert bwd_bs(layout=None) == 1
+    assert fwd_bs(block=64) == 3                     # 128-token blocks only
+    assert bwd_bs(block=256) == 3
+    assert fwd_bs(dtype=U.FP32) == 3                 # bf16 only
+    assert fwd_bs(Hkv=3) == 2
+    assert fwd_bs(q=None) == 1
+    assert bwd_bs(ws_bytes=8) == 6
+    # the layout is an input: an output over it is refused (o and lse, dq and dv)
+    assert fwd_bs(layout=A + 3 * GB + 256) == 5
+    assert fwd_bs(layout=A + 4 * GB) == 5
+    assert bwd_bs(layout=A + 6 * GB + 100) == 5
+    assert bwd_bs(layout=A + 8 * GB) == 5
+    # the dK/dV kernel lists at most 8192 (query head, query block) pairs per key block
+    assert bwd_bs(L=1 << 20, Hq=64, Hkv=8, P=8) == 3     # 8 x 8192 pairs
+    assert bwd_bs(Hq=64, Hkv=4, P=4) == 3                # 16 query heads per K/V head

@@ -19,7 +19,9 @@ Grouped-query workloads run K and V through the K/V layout change (and dK,
 dV through its gradient form); a K/V head's dK/dV columns are checked
 against the sum of its query heads' oracle columns. The cross-attention
 workload (queries and keys of different lengths) is bidirectional, so it has
-no causal prefix; its dK/dV columns are checked on its first head.
+no causal prefix; its dK/dV columns are checked on its first head. The
+block-sparse workload runs the block-sparse entry points with rank 0's seeded
+block layout, and every oracle value is formed under the same layout.
 """
 import gc
 
@@ -28,14 +30,14 @@ import pytest
 
 import exact_attention_ulysses_amd as U
 import oracle
-from workloads import WORKLOADS, device_tensor, stress_positions
+from workloads import WORKLOADS, block_layout, device_tensor, stress_positions
 
 from gpu_common import bf16_ulp, check_close, shared_head_allowed, to_f64, to_host_bits, torch_mod
 
 pytestmark = pytest.mark.gpu
 
 NAMES = ["gpt1.2b-L32k-fwd", "gpt7b-L131k", "gpt30b-L262k", "L1m", "gqa8-L131k", "gqa2-L131k",
-         "cross-L16k-L131k"]
+         "cross-L16k-L131k", "bsparse-L131k"]
 
 
 def _kv(n):
@@ -75,13 +77,24 @@ class Run:
         r0 = {n: self.head[n][0] for n in self.ins}
         o0 = {n: self.ohead[n][0] for n in self.outs}
         self.lse = torch.empty((B, Hh, L), dtype=torch.float32, device="cuda")
+        # block layout of rank 0's heads (block-sparse workloads)
+        self.layout = block_layout(wl, heads=range(Hh)) if wl.block else None
+        lay = torch.from_numpy(self.layout).to("cuda") if wl.block else None
         print(f"[{key}] attention", flush=True)
-        U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], self.lse, B, L, Lk, H, Hk, d, P, wl.causal)
+        if wl.block:
+            U.ulysses_attn_fwd_block_sparse(r0["q"], r0["k"], r0["v"], o0["o"], self.lse, lay, B, L, H, Hk, d, P,
+                                            wl.causal)
+        else:
+            U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], self.lse, B, L, Lk, H, Hk, d, P, wl.causal)
         if wl.backward:
             ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, wl.causal),
                              dtype=torch.uint8, device="cuda")
-            U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], self.lse, o0["dq"], o0["dk"],
-                                   o0["dv"], ws, B, L, Lk, H, Hk, d, P, wl.causal)
+            if wl.block:
+                U.ulysses_attn_bwd_block_sparse(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], self.lse, o0["dq"],
+                                                o0["dk"], o0["dv"], lay, ws, B, L, H, Hk, d, P, wl.causal)
+            else:
+                U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], self.lse, o0["dq"], o0["dk"],
+                                       o0["dv"], ws, B, L, Lk, H, Hk, d, P, wl.causal)
         self.oseq = {}
         for n in self.outs:
             self.oseq[n] = torch.empty(wl.shape_of(n[1:] if _kv(n) else "q"), dtype=torch.bfloat16,
@@ -200,7 +213,11 @@ def test_forward_sampled_rows(key):
     for h in range(wl.Hp):
         j = h // run.G
         for kind, rows in (("edge", edge_rows(wl, h)), ("uniform", uniform_rows(wl, h))):
-            ref = oracle.attn_rows(q[0, :, h], k[0, :, j], v[0, :, j], rows, wl.causal)
+            if wl.block:
+                ref = oracle.attn_rows_block_sparse(q[0, :, h], k[0, :, j], v[0, :, j], rows, run.layout[h], wl.block,
+                                                    wl.causal)
+            else:
+                ref = oracle.attn_rows(q[0, :, h], k[0, :, j], v[0, :, j], rows, wl.causal)
             check_close(f"O {kind} rows head {h}", o[0, rows, h], ref["o"], "bf16", fro=(kind == "uniform"))
             assert np.max(np.abs(lse[0, h, rows] - ref["lse"])) <= 1e-3
 
@@ -216,7 +233,13 @@ def test_causal_prefix_matches_full_run_and_oracle(key):
     assert B == 1 and all(t.is_contiguous() for t in r0.values())
     o = torch.empty((B, Lp, Hh, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hh, Lp), dtype=torch.float32, device="cuda")
-    U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o, lse, B, Lp, Lp, H, Hk, d, P, True)
+    if wl.block:   # the prefix's blocks keep their layout entries
+        nbp = Lp // wl.block
+        lay_p = np.ascontiguousarray(run.layout[:, :nbp, :nbp])
+        lay_dev = torch.from_numpy(lay_p).to("cuda")
+        U.ulysses_attn_fwd_block_sparse(r0["q"], r0["k"], r0["v"], o, lse, lay_dev, B, Lp, H, Hk, d, P, True)
+    else:
+        U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o, lse, B, Lp, Lp, H, Hk, d, P, True)
     full_o = run.ohead["o"][0][:, :Lp]
     assert torch.equal(o.view(torch.int16), full_o.view(torch.int16)), "prefix rows differ from the full run"
     assert torch.equal(lse, run.lse[:, :, :Lp].contiguous())
@@ -227,12 +250,20 @@ def test_causal_prefix_matches_full_run_and_oracle(key):
         dk, dv = torch.empty_like(r0["k"]), torch.empty_like(r0["v"])
         ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, Lp, Lp, H, Hk, d, P), dtype=torch.uint8,
                          device="cuda")
-        U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, ws, B, Lp, Lp, H, Hk, d, P,
-                               True)
+        if wl.block:
+            U.ulysses_attn_bwd_block_sparse(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, lay_dev, ws, B,
+                                            Lp, H, Hk, d, P, True)
+        else:
+            U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, ws, B, Lp, Lp, H, Hk, d,
+                                   P, True)
         # dQ rows depend only on earlier keys: equal to the full run's
         assert torch.equal(dq.view(torch.int16), run.ohead["dq"][0][:, :Lp].view(torch.int16))
-        dq_r, dk_r, dv_r = oracle.attn_bwd_gqa(q, k, v, do, True)
-        o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
+        if wl.block:
+            dq_r, dk_r, dv_r = oracle.attn_bwd_block_sparse(q, k, v, do, lay_p, wl.block, True)
+            o_r, lse_r = oracle.attn_fwd_block_sparse(q, k, v, lay_p, wl.block, True)
+        else:
+            dq_r, dk_r, dv_r = oracle.attn_bwd_gqa(q, k, v, do, True)
+            o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
         check_close("dQ prefix", to_f64(dq, "bf16"), dq_r, "bf16")
         G = run.G
         if G == 1:
@@ -246,6 +277,8 @@ def test_causal_prefix_matches_full_run_and_oracle(key):
             allowed = {nm: shared_head_allowed(parts[nm], want, "bf16") for nm, want in (("dK", dk_r), ("dV", dv_r))}
         check_close("dK prefix problem", to_f64(dk, "bf16"), dk_r, "bf16", allowed=allowed["dK"])
         check_close("dV prefix problem", to_f64(dv, "bf16"), dv_r, "bf16", allowed=allowed["dV"])
+    elif wl.block:
+        o_r, lse_r = oracle.attn_fwd_block_sparse(q, k, v, lay_p, wl.block, True)
     else:
         o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
     check_close("O prefix", to_f64(o, "bf16"), o_r, "bf16")
@@ -266,7 +299,11 @@ def test_backward_sampled_rows_and_columns(key):
     for h in range(wl.Hp):
         j = h // G
         for kind, rows in (("edge", edge_rows(wl, h)), ("uniform", uniform_rows(wl, h))):
-            ref = oracle.attn_rows(q[0, :, h], k[0, :, j], v[0, :, j], rows, wl.causal, do=do[0, :, h])
+            if wl.block:
+                ref = oracle.attn_rows_block_sparse(q[0, :, h], k[0, :, j], v[0, :, j], rows, run.layout[h], wl.block,
+                                                    wl.causal, do=do[0, :, h])
+            else:
+                ref = oracle.attn_rows(q[0, :, h], k[0, :, j], v[0, :, j], rows, wl.causal, do=do[0, :, h])
             check_close(f"dQ {kind} rows head {h}", dq[0, rows, h], ref["dq"], "bf16", fro=(kind == "uniform"))
     # bidirectional attention: every query row sees every column, so a column
     # costs a full pass over the rows; check the first K/V head there
@@ -274,8 +311,12 @@ def test_backward_sampled_rows_and_columns(key):
     for j in kv_heads:
         parts_k, parts_v = [], []
         for h in range(j * G, (j + 1) * G):
-            c, dk_r, dv_r = oracle.attn_dkv_cols(q[0, :, h], k[0, :, j], v[0, :, j], do[0, :, h], cols, wl.causal,
-                                                 row_block=64)
+            if wl.block:
+                c, dk_r, dv_r = oracle.attn_dkv_cols_block_sparse(q[0, :, h], k[0, :, j], v[0, :, j], do[0, :, h],
+                                                                  cols, run.layout[h], wl.block, wl.causal)
+            else:
+                c, dk_r, dv_r = oracle.attn_dkv_cols(q[0, :, h], k[0, :, j], v[0, :, j], do[0, :, h], cols,
+                                                     wl.causal, row_block=64)
             parts_k.append(dk_r)
             parts_v.append(dv_r)
         if G == 1:

@@ -628,7 +628,10 @@ def test_block_sparse_brute_force_and_sampled_rows():
         want = [sum(wj * v[j, e] for wj, j in zip(w, js)) / z for e in range(d)]
         np.testing.assert_allclose(o[i], want, rtol=1e-12, atol=1e-13)
         assert abs(lse[i] - math.log(z)) < 1e-12
-    dq, *_ = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, True)
+    dq, dk, dv, *_ = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, True)
+    c, dkc, dvc = oracle.attn_dkv_cols_block_sparse(q, k, v, do, [39, 31, 30, 9, 0], lay, block, True)
+    np.testing.assert_allclose(dkc, dk[c], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[c], rtol=0, atol=1e-12)
     rows = [0, 7, 8, 23, 39]
     r = oracle.attn_rows_block_sparse(q, k, v, rows, lay, block, True, do=do)
     np.testing.assert_allclose(r["o"], o[rows], rtol=0, atol=1e-13)
