@@ -139,7 +139,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=49152,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
                     help="prefix length of one head that the fp64 oracle runs fwd+bwd on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 runs)")
