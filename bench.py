@@ -230,8 +230,9 @@ def main():
     ohead = {n: device_tensor(wl, "fill_" + n, dev) for n in outs}
     oseq = {n: torch.empty(wl.shape_of(n[1:] if kv(n) else "q"), dtype=torch.bfloat16, device=dev) for n in outs}
     lse = torch.empty((B, Hh, L), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, causal)),
-                     dtype=torch.uint8, device=dev)
+    ws_bytes = (U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, H, Hk, d, P, causal) if wl.block
+                else U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, causal))
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     # block-sparse workloads: rank 0's seeded block layout
     layout_host = block_layout(wl, heads=range(Hh)) if wl.block else None
     layout = torch.from_numpy(layout_host).to(dev) if wl.block else None

@@ -32,6 +32,7 @@ EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_kv
            "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
            "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa", "ulysses_attn_bwd_gqa_workspace_bytes",
            "ulysses_attn_fwd_block_sparse", "ulysses_attn_bwd_block_sparse",
+           "ulysses_attn_bwd_block_sparse_workspace_bytes",
            "ulysses_status_string", "ulysses_last_hip_error")
 
 
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.ulysses_attn_bwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp, sz,
                                                 i64, i64, i64, i64, i64, i64, ci, ci, vp]
     L.ulysses_attn_bwd_block_sparse.restype = ci
+    L.ulysses_attn_bwd_block_sparse_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, ci]
+    L.ulysses_attn_bwd_block_sparse_workspace_bytes.restype = sz
     L.ulysses_status_string.argtypes = [ci]
     L.ulysses_status_string.restype = ctypes.c_char_p
     L.ulysses_last_hip_error.argtypes = []
@@ -239,7 +242,7 @@ def ulysses_attn_fwd_block_sparse(q, k, v, o, lse, layout, B: int, L: int, H_q: 
 def ulysses_attn_bwd_block_sparse(q, k, v, o, d_o, lse, dq, dk, dv, layout, workspace, B: int, L: int, H_q: int,
                                   H_kv: int, d_h: int, P: int, causal: bool = True, block: int = SPARSE_BLOCK,
                                   stream=None) -> None:
-    """dQ, dK, dV of ulysses_attn_fwd_block_sparse; workspace as for ulysses_attn_bwd_gqa (L_q = L_kv = L)."""
+    """dQ, dK, dV of ulysses_attn_fwd_block_sparse; workspace of ulysses_attn_bwd_block_sparse_workspace_bytes."""
     torch = _torch()
     nq, nk, nl = _gqa_sizes("ulysses_attn_bwd_block_sparse", B, L, L, H_q, H_kv, d_h, P)
     if not workspace.is_cuda or not workspace.is_contiguous():
@@ -252,6 +255,13 @@ def ulysses_attn_bwd_block_sparse(q, k, v, o, d_o, lse, dq, dk, dv, layout, work
         _layout(layout, H_q, P, L, block), block, workspace.data_ptr(), wbytes, B, L, H_q, H_kv, d_h, P,
         int(bool(causal)), dtype_code(q), _stream(stream))
     _check(st, "ulysses_attn_bwd_block_sparse")
+
+
+def ulysses_attn_bwd_block_sparse_workspace_bytes(B: int, L: int, H_q: int, H_kv: int, d_h: int, P: int,
+                                                  causal: bool = True, dtype: int = BF16,
+                                                  block: int = SPARSE_BLOCK) -> int:
+    return int(lib().ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, H_q, H_kv, d_h, P, block,
+                                                                   int(bool(causal)), dtype))
 
 
 def ulysses_attn_fwd(q, k, v, o, lse, B: int, L: int, H: int, d_h: int, P: int, causal: bool = True,
@@ -297,4 +307,5 @@ __all__ = ["lib", "LIB_PATH", "BF16", "FP32", "UlyssesError", "EXPORTS", "kv_loc
            "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad", "ulysses_attn_fwd",
            "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa",
            "ulysses_attn_bwd_gqa_workspace_bytes", "ulysses_attn_fwd_block_sparse", "ulysses_attn_bwd_block_sparse",
+           "ulysses_attn_bwd_block_sparse_workspace_bytes",
            "SPARSE_BLOCK"]

@@ -64,6 +64,138 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block layouts: the dK/dV work plan. The column kernel lists the active
+// (query head, query block) pairs of every layout column once, in the order
+// the dK/dV kernel visits them, so that its workgroups copy a contiguous list
+// instead of scanning a layout column (one byte every nb bytes). A column that
+// many query blocks attend (a global block) would make one dK/dV workgroup
+// walk all of them: a single workgroup plans the work (plan kernel), cutting
+// columns with more than kSparseChunk pairs into equal chunks, each chunk a
+// work item of its own, as long as the partial-sum slots of the workspace
+// last (later heavy columns stay whole); the dK/dV kernel writes a split
+// column's chunks as fp32 partial sums and the reduce kernel adds them in
+// chunk order. No atomics: the result does not depend on timing.
+// ---------------------------------------------------------------------------
+
+// Grid: one workgroup (one wave) per layout column hk * nb + kb.
+template <bool CAUSAL>
+__global__ __launch_bounds__(64) void bwd_sparse_columns_kernel(const uint8_t* __restrict__ layout, int nb, int G,
+                                                                int nlcol, SparsePlan plan) {
+  const int col = blockIdx.x;
+  if (col >= nlcol) return;
+  const int lane = threadIdx.x;
+  const int hk = col / nb, kb = col - hk * nb;
+  uint16_t* out = plan.colpairs + (size_t)col * G * nb;
+  int c = 0;
+  for (int g = 0; g < G; ++g) {
+    const uint8_t* cp = layout + (size_t)(hk * G + g) * nb * nb + kb;
+    for (int base = CAUSAL ? kb : 0; base < nb; base += 64) {
+      const int i = base + lane;
+      const bool act = i < nb && cp[(size_t)i * nb] != 0;
+      const uint64_t m = __ballot(act);
+      if (act) out[c + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = (uint16_t)(g * 8192 + i);
+      c += __builtin_popcountll(m);
+    }
+  }
+  if (lane == 0) plan.cnt[col] = c;
+}
+
+// One workgroup of 256 threads; thread t plans the work columns of a
+// contiguous range (work column c has the pairs of layout column c mod nlcol).
+__global__ __launch_bounds__(256) void bwd_sparse_plan_kernel(int ncol, int nlcol, SparsePlan plan) {
+  __shared__ int s_slots[256], s_items[256], s_splits[256];
+  const int t = threadIdx.x;
+  const int per = (ncol + 255) / 256;
+  const int c0 = min(ncol, t * per), c1 = min(ncol, c0 + per);
+  // slots each column would need if split (0 when it stays whole)
+  auto demand = [&](int c) {
+    const int n = plan.cnt[c % nlcol];
+    return n > kSparseChunk ? (n + kSparseChunk - 1) / kSparseChunk : 0;
+  };
+  auto exclusive_prefix = [&](int* a) {   // serial over 256 values
+    int acc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int x = a[i];
+      a[i] = acc;
+      acc += x;
+    }
+    return acc;
+  };
+  int my_slots = 0;
+  for (int c = c0; c < c1; ++c) my_slots += demand(c);
+  s_slots[t] = my_slots;
+  __syncthreads();
+  if (t == 0) exclusive_prefix(s_slots);
+  __syncthreads();
+  // a column is split when its whole demand fits the slots in column order
+  int slot = s_slots[t], my_items = 0, my_splits = 0;
+  for (int c = c0; c < c1; ++c) {
+    const int dmd = demand(c);
+    const bool split = dmd > 0 && slot + dmd <= kSparseSlots;
+    my_items += split ? dmd : 1;
+    my_splits += split;
+    slot += dmd;
+  }
+  s_items[t] = my_items;
+  s_splits[t] = my_splits;
+  __syncthreads();
+  if (t == 0) {
+    plan.header[0] = exclusive_prefix(s_items);
+    plan.header[1] = exclusive_prefix(s_splits);
+  }
+  __syncthreads();
+  slot = s_slots[t];
+  int item = s_items[t], sp = s_splits[t];
+  for (int c = c0; c < c1; ++c) {
+    const int dmd = demand(c);
+    const bool split = dmd > 0 && slot + dmd <= kSparseSlots;
+    const int nch = split ? dmd : 1;
+    for (int j = 0; j < nch; ++j) plan.items[item + j] = make_int4(c, j, nch, split ? slot : 0);
+    if (split) {
+      plan.split_col[sp] = c;
+      plan.split_slot[sp] = slot;
+      plan.split_nch[sp] = nch;
+      ++sp;
+    }
+    item += nch;
+    slot += dmd;
+  }
+}
+
+// dK, dV of the split columns: the chunks' partial sums added in chunk order.
+// Work unit u: split column u / (D/4), and 1024/D of its 256 [dK | dV] rows
+// from row (1024/D) * (u mod (D/4)) on; each thread sums one 4-float group.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan, int nb, int Lk, int Hk,
+                                                                __bf16* __restrict__ dk, __bf16* __restrict__ dv,
+                                                                float scale) {
+  constexpr int UNITS = D / 4, ROWS = 1024 / D;   // units per split column, rows per unit
+  const int nunits = plan.header[1] * UNITS;
+  const size_t rsk = (size_t)Hk * D;
+  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const int sp = u / UNITS;
+    const int col = plan.split_col[sp], slot = plan.split_slot[sp], nch = plan.split_nch[sp];
+    const int kb = col % nb, hb = col / nb;
+    const int b = hb / Hk, hk = hb - b * Hk;
+    const int row = (u - sp * UNITS) * ROWS + (int)threadIdx.x / (D / 4);   // of [dK | dV][128]
+    const int c4 = ((int)threadIdx.x % (D / 4)) * 4;
+    const int which = row >> 7, r = row & 127;
+    f32x4 acc = f32x4{};
+    for (int j = 0; j < nch; ++j)
+      acc += *reinterpret_cast<const f32x4*>(plan.partials + ((size_t)(slot + j) * 256 + row) * D + c4);
+    const int key = kb * 128 + r;
+    if (key < Lk) {
+      __bf16* dst = (which ? dv : dk) + ((size_t)b * Lk * Hk + hk) * D + (size_t)key * rsk + c4;
+      const float sc = which ? 1.f : scale;
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[i] * sc);
+      *reinterpret_cast<bf16x4*>(dst) = o;
+    }
+  }
+}
+
 // dK/dV as producer/consumer wave pairs. A workgroup owns 128 keys and has 8
 // waves: producer wave w (0..3) and consumer wave w+4 share keys 32w..32w+31
 // and, with the usual in-order placement of a workgroup's waves on the four
@@ -80,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
-    float scale, const uint8_t* __restrict__ layout, int nb) {
+    float scale, const uint8_t* __restrict__ layout, int nb, const SparsePlan plan) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256, RSTEP = 256 / CPR;
   constexpr int ST = Stride<D>::both;  // Q and dO tiles are read along rows and transposed
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
@@ -89,17 +221,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float dls[2][BQ];
   // hand-over: [buffer][producer][P or dS][half u * 2 + chunk c][lane]
   __shared__ __attribute__((aligned(16))) bf16x8 hand[2][4][2][4][64];
-  // block layouts: the active (query head g, query block i) pairs of this key
-  // block, g * 8192 + i, in visiting order
+  // block layouts: this work item's (query head g, query block i) pairs,
+  // g * 8192 + i, in visiting order
   __shared__ uint16_t pairs[SPARSE ? kMaxSparsePairs : 1];
-  __shared__ int npairs;
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave < 4;
   const int pw = wave & 3;                 // key group of this wave (shared by the pair)
-  const int kb = blockIdx.x / nhb;         // key block 0 has the most query tiles under the causal mask
-  const int hb = blockIdx.x % nhb;         // (batch, key head) pair
+  // dense: key block 0 has the most query tiles under the causal mask;
+  // block layouts: the planned work item (key block column, chunk of its pairs)
+  int col = blockIdx.x, chunk = 0, nchunk = 1, slot = 0;
+  if constexpr (SPARSE) {
+    if ((int)blockIdx.x >= plan.header[0]) return;   // no work item (uniform for the workgroup)
+    const int4 it = plan.items[blockIdx.x];
+    col = it.x;
+    chunk = it.y;
+    nchunk = it.z;
+    slot = it.w;
+  }
+  const int kb = SPARSE ? col % (nb) : (int)blockIdx.x / nhb;
+  const int hb = SPARSE ? col / (nb) : (int)blockIdx.x % nhb;   // (batch, key head) pair
   const int b = hb / Hk, hk = hb - b * Hk;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;   // row strides
   // query heads hk*G .. hk*G + G-1 share this key head; g selects one of them
@@ -117,25 +259,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   // under the causal mask only the first two query tiles reach above a key of this block
   const int nmask = CAUSAL ? min(nqt, 2) : 0;
   if constexpr (SPARSE) {
-    // wave 0 lists the active query blocks of this key block's layout column for
-    // each query head of the group (causal: from the diagonal block on); each
-    // query block is two 64-row query tiles
-    if (wave == 0) {
-      int cnt = 0;
-      for (int g = 0; g < G; ++g) {
-        const uint8_t* col = layout + (size_t)(hk * G + g) * nb * nb + kb;
-        for (int base = CAUSAL ? kb : 0; base < nb; base += 64) {
-          const int i = base + lane;
-          const bool act = i < nb && col[(size_t)i * nb] != 0;
-          const uint64_t m = __ballot(act);
-          if (act) pairs[cnt + __builtin_popcountll(m & ((uint64_t(1) << lane) - 1))] = (uint16_t)(g * 8192 + i);
-          cnt += __builtin_popcountll(m);
-        }
-      }
-      if (lane == 0) npairs = cnt;
-    }
+    // this work item's share of the layout column's listed pairs (query head,
+    // query block; causal: from the diagonal block on): chunk `chunk` of
+    // `nchunk` equal parts, copied to LDS; each query block is two 64-row
+    // query tiles
+    const int lcol = hk * nb + kb;
+    const int npairs = plan.cnt[lcol];
+    const int per = (npairs + nchunk - 1) / nchunk;
+    const int pair0 = chunk * per;
+    const int n = max(0, min(npairs, pair0 + per) - pair0);
+    const uint16_t* src = plan.colpairs + (size_t)lcol * G * nb + pair0;
+    for (int i = tid; i < n; i += 512) pairs[i] = src[i];
+    nsteps = 2 * n;
     __syncthreads();
-    nsteps = 2 * npairs;
   }
 
   // staging of Q, dO, lse, delta by the producer waves (threads 0..255) through
@@ -305,7 +441,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       __syncthreads();
       __syncthreads();
     }
-    if (key < Lk) {
+    if (SPARSE && nchunk > 1) {
+      // one chunk of a split column: unscaled fp32 partial sums, [dK | dV][128 keys][D],
+      // summed in chunk order by the reduce kernel
+      float* part = plan.partials + (size_t)(slot + chunk) * 2 * 128 * D;
+      const int kr = key - kb * 128;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4 k4, v4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            k4[i] = dkacc[dt][4 * a + i];
+            v4[i] = dvacc[dt][4 * a + i];
+          }
+          *reinterpret_cast<f32x4*>(part + (size_t)kr * D + 32 * dt + 8 * a + 4 * hl) = k4;
+          *reinterpret_cast<f32x4*>(part + (size_t)(128 + kr) * D + 32 * dt + 8 * a + 4 * hl) = v4;
+        }
+      }
+    } else if (key < Lk) {
       __bf16* dkrow = dk + koff + (size_t)key * rsk;
       __bf16* dvrow = dv + koff + (size_t)key * rsk;
 #pragma unroll
@@ -619,6 +774,34 @@ hipError_t launch_delta(const T* o, const T* d_o, float* delta, const AttnShape&
   return hipGetLastError();
 }
 
+inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace: delta [B][Hq][Lq] fp32, then (block layouts only) the layout
+// columns' pair counts and lists, the plan and the partial-sum slots, each
+// 256-byte aligned.
+size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char* base) {
+  const size_t ncol = (size_t)s.B * s.Hk * ((s.Lk + kSparseBlock - 1) / kSparseBlock);
+  size_t off = round256((size_t)s.B * s.Hq * s.Lq * sizeof(float));
+  if (!sparse) return off;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += round256(bytes);
+    return p;
+  };
+  const size_t nb = (s.Lk + kSparseBlock - 1) / kSparseBlock, nlcol = (size_t)s.Hk * nb;
+  SparsePlan pl;
+  pl.cnt = (int*)take(nlcol * sizeof(int));
+  pl.colpairs = (uint16_t*)take(nlcol * (s.Hq / s.Hk) * nb * sizeof(uint16_t));
+  pl.header = (int*)take(4 * sizeof(int));
+  pl.items = (int4*)take((ncol + kSparseSlots) * sizeof(int4));
+  pl.split_col = (int*)take(kMaxSplitColumns * sizeof(int));
+  pl.split_slot = (int*)take(kMaxSplitColumns * sizeof(int));
+  pl.split_nch = (int*)take(kMaxSplitColumns * sizeof(int));
+  pl.partials = (float*)take((size_t)kSparseSlots * 2 * 128 * s.D * sizeof(float));
+  if (plan) *plan = pl;
+  return off;
+}
+
 template <int D, bool CAUSAL>
 hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
                     void* dq, void* dk, void* dv, float* delta, const AttnShape& s, hipStream_t stream) {
@@ -630,14 +813,24 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
   const int nkhb = s.B * s.Hk;
   const int nkb = (s.Lk + 127) / 128;
   const int nb = (s.Lk + kSparseBlock - 1) / kSparseBlock;
-  if (s.layout)
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb);
-  else
+  if (s.layout) {
+    SparsePlan plan;
+    workspace_layout(s, true, &plan, reinterpret_cast<char*>(delta));
+    const int ncol = nkb * nkhb, nlcol = s.Hk * nb;
+    hipLaunchKernelGGL((bwd_sparse_columns_kernel<CAUSAL>), dim3((unsigned)nlcol), dim3(64), 0, stream, s.layout, nb,
+                       G, nlcol, plan);
+    hipLaunchKernelGGL(bwd_sparse_plan_kernel, dim3(1), dim3(256), 0, stream, ncol, nlcol, plan);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)(ncol + kSparseSlots)), dim3(512), 0,
+                       stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb, plan);
+    hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D>), dim3(1024), dim3(256), 0, stream, plan, nb, s.Lk, s.Hk,
+                       (__bf16*)dk, (__bf16*)dv, scale);
+  } else {
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0);
+                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0,
+                       SparsePlan{});
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nhb = s.B * s.Hq;
@@ -676,9 +869,8 @@ hipError_t bwd_f32(const float* q, const float* k, const float* v, const float* 
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(const AttnShape& s) {
-  const size_t delta = (size_t)s.B * s.Hq * s.Lq * sizeof(float);
-  return (delta + 255) / 256 * 256;
+size_t attn_bwd_workspace_bytes(const AttnShape& s, bool sparse) {
+  return workspace_layout(s, sparse, nullptr, nullptr);
 }
 
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* d_o,

@@ -22,6 +22,26 @@ constexpr int kSparseBlock = 128;   // tokens per layout block
 // most 8 query heads per K/V head.
 constexpr int kMaxSparsePairs = 8192;
 constexpr int kMaxSparseGroup = 8;
+// Heavily attended key block columns are cut into chunks of this many
+// (query head, query block) pairs, using at most kSparseSlots partial-sum
+// slots of [2][128][d_h] fp32 each; a split column has at least two chunks.
+constexpr int kSparseChunk = 32;
+constexpr int kSparseSlots = 512;
+constexpr int kMaxSplitColumns = kSparseSlots / 2;
+
+// The backward pass's work plan for block layouts, in the workspace. A layout
+// column is (K/V head hk, key block kb), index hk * nb + kb, shared by the
+// batch; a work column adds the batch: (b * H_kv + hk) * nb + kb.
+struct SparsePlan {
+  int* cnt;               // [H_kv * nb] active pairs of each layout column
+  uint16_t* colpairs;     // [H_kv * nb][G * nb] those pairs, g * 8192 + i, ascending
+  int* header;            // [0]: dK/dV work items, [1]: split work columns
+  int4* items;            // (work column, chunk, chunks of the column, first slot)
+  int* split_col;         // [kMaxSplitColumns] work column of each split
+  int* split_slot;        // its first slot
+  int* split_nch;         // its chunks (= slots)
+  float* partials;        // [kSparseSlots][2][128][d_h]
+};
 
 struct LayoutScan {
   const uint8_t* p;   // entry 0 of the row or column

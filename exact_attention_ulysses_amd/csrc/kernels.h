@@ -41,8 +41,9 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
 hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                                const AttnShape& s, hipStream_t stream);
 
-// workspace layout: delta [B][Hq][Lq] fp32, then (256-byte aligned) nothing else
-size_t attn_bwd_workspace_bytes(const AttnShape& s);
+// workspace layout: delta [B][Hq][Lq] fp32; with a block layout also the
+// backward's work plan and partial-sum slots (all 256-byte aligned)
+size_t attn_bwd_workspace_bytes(const AttnShape& s, bool sparse);
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* d_o, const float* lse, void* dq, void* dk, void* dv,
                                 void* workspace, const AttnShape& s, hipStream_t stream);

@@ -150,12 +150,18 @@ int64_t lse_bytes(const AttnShape& s) { return (int64_t)s.B * s.Hq * s.Lq * 4; }
 
 // Block layouts: 128-token blocks, bf16, self-attention; the dK/dV kernel's
 // pair list bounds the query heads per K/V head and the blocks per column.
+int sparse_supported(int64_t block, int64_t Lq, int64_t Lk, int dtype, const AttnShape& s, bool backward) {
+  if (block != kSparseBlock || dtype != ULYSSES_BF16 || Lq != Lk) return ULYSSES_UNSUPPORTED;
+  const int64_t nb = (Lk + kSparseBlock - 1) / kSparseBlock, G = s.Hq / s.Hk;
+  if (backward && (G > kMaxSparseGroup || G * nb > kMaxSparsePairs)) return ULYSSES_UNSUPPORTED;
+  return ULYSSES_OK;
+}
+
 int sparse_dims(const uint8_t* layout, int64_t block, int64_t Lq, int64_t Lk, int dtype, AttnShape* s,
                 bool backward) {
   if (!layout) return ULYSSES_INVALID_ARGUMENT;
-  if (block != kSparseBlock || dtype != ULYSSES_BF16 || Lq != Lk) return ULYSSES_UNSUPPORTED;
-  const int64_t nb = (Lk + kSparseBlock - 1) / kSparseBlock, G = s->Hq / s->Hk;
-  if (backward && (G > kMaxSparseGroup || G * nb > kMaxSparsePairs)) return ULYSSES_UNSUPPORTED;
+  const int st = sparse_supported(block, Lq, Lk, dtype, *s, backward);
+  if (st != ULYSSES_OK) return st;
   s->layout = layout;
   return ULYSSES_OK;
 }
@@ -194,7 +200,7 @@ size_t attn_ws_entry(int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv,
                      int causal, int dtype) {
   AttnShape s;
   if (attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s) != ULYSSES_OK) return 0;
-  return attn_bwd_workspace_bytes(s);
+  return attn_bwd_workspace_bytes(s, false);
 }
 
 int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -213,7 +219,7 @@ int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, c
   for (const void* p : al16)
     if (!aligned(p, 16)) return ULYSSES_MISALIGNED;
   if (!aligned(lse, 4)) return ULYSSES_MISALIGNED;
-  const size_t need = attn_bwd_workspace_bytes(s);
+  const size_t need = attn_bwd_workspace_bytes(s, layout != nullptr);
   if (workspace_bytes < need) return ULYSSES_WORKSPACE_TOO_SMALL;
   const int64_t tq = q_bytes(s, dtype), tk = k_bytes(s, dtype);
   const Range outs[4] = {range_of(dq, tq), range_of(dk, tk), range_of(dv, tk), range_of(workspace, (int64_t)need)};
@@ -284,6 +290,14 @@ size_t ulysses_attn_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t
 size_t ulysses_attn_bwd_gqa_workspace_bytes(int64_t B, int64_t L_q, int64_t L_kv, int64_t H_q, int64_t H_kv,
                                             int64_t d_h, int64_t P, int causal, int dtype) {
   return attn_ws_entry(B, L_q, L_kv, H_q, H_kv, d_h, P, causal, dtype);
+}
+
+size_t ulysses_attn_bwd_block_sparse_workspace_bytes(int64_t B, int64_t L, int64_t H_q, int64_t H_kv, int64_t d_h,
+                                                     int64_t P, int64_t block, int causal, int dtype) {
+  AttnShape s;
+  if (attn_dims(B, L, L, H_q, H_kv, d_h, P, causal, dtype, &s) != ULYSSES_OK) return 0;
+  if (sparse_supported(block, L, L, dtype, s, true) != ULYSSES_OK) return 0;
+  return attn_bwd_workspace_bytes(s, true);
 }
 
 int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,

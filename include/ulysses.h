@@ -214,9 +214,15 @@ size_t ulysses_attn_bwd_gqa_workspace_bytes(int64_t B, int64_t L_q, int64_t L_kv
  * with causal = 1, j <= i (entries above the block diagonal are then ignored).
  * A query row that sees no key gets O = 0 and lse = -inf, and passes no
  * gradient. bf16 only (ULYSSES_UNSUPPORTED otherwise). The backward pass also
- * needs (H_q/H_kv) <= 8 and (H_q/H_kv) * nb <= 8192 (UNSUPPORTED otherwise);
- * its workspace is ulysses_attn_bwd_gqa_workspace_bytes(B, L, L, ...).
- * Only the active blocks are computed.
+ * needs (H_q/H_kv) <= 8 and (H_q/H_kv) * nb <= 8192 (UNSUPPORTED otherwise)
+ * and a workspace of at least ulysses_attn_bwd_block_sparse_workspace_bytes
+ * bytes (ULYSSES_WORKSPACE_TOO_SMALL otherwise): besides the per-row delta it
+ * holds each layout column's list of active (query head, query block) pairs
+ * (2 bytes per layout entry), a work plan that cuts key blocks attended by
+ * many query blocks into chunks handled by separate workgroups, and at most
+ * 512 fp32 partial-sum slots of 2 x 128 x d_h that a last pass adds in a
+ * fixed order, so results do not depend on scheduling. Only the active blocks
+ * are computed.
  */
 int ulysses_attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                   const uint8_t* layout, int64_t block,
@@ -230,6 +236,12 @@ int ulysses_attn_bwd_block_sparse(const void* q, const void* k, const void* v, c
                                   void* workspace, size_t workspace_bytes,
                                   int64_t B, int64_t L, int64_t H_q, int64_t H_kv, int64_t d_h, int64_t P,
                                   int causal, int dtype, void* stream);
+
+/* Workspace bytes for ulysses_attn_bwd_block_sparse with these sizes; 0 if
+ * they are invalid or unsupported. */
+size_t ulysses_attn_bwd_block_sparse_workspace_bytes(int64_t B, int64_t L, int64_t H_q, int64_t H_kv,
+                                                     int64_t d_h, int64_t P, int64_t block, int causal,
+                                                     int dtype);
 
 /* Static, NUL-terminated name of a status code ("ULYSSES_OK", ...). */
 const char* ulysses_status_string(int status);

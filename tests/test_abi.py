@@ -230,7 +230,7 @@ def bwd_bs(layout=A + 12 * GB, block=128, ws_bytes=None, B=1, L=1024, Hq=32, Hkv
     p = {n: A + i * GB for i, n in enumerate(names)}
     p.update(ptrs)
     if ws_bytes is None:
-        ws_bytes = U.lib().ulysses_attn_bwd_gqa_workspace_bytes(B, L, L, Hq, Hkv, d, P, causal, dtype)
+        ws_bytes = U.lib().ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, Hq, Hkv, d, P, block, causal, dtype)
     return U.lib().ulysses_attn_bwd_block_sparse(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"],
                                                  p["dv"], layout, block, p["ws"], ws_bytes, B, L, Hq, Hkv, d, P,
                                                  causal, dtype, None)
@@ -245,6 +245,9 @@ def test_block_sparse_validation():
     assert fwd_bs(Hkv=3) == 2
     assert fwd_bs(q=None) == 1
     assert bwd_bs(ws_bytes=8) == 6
+    # the dense workspace (delta only) is too small for the block-sparse plan
+    dense = U.lib().ulysses_attn_bwd_gqa_workspace_bytes(1, 1024, 1024, 32, 8, 128, 8, 1, U.BF16)
+    assert bwd_bs(ws_bytes=dense) == 6
     # the layout is an input: an output over it is refused (o and lse, dq and dv)
     assert fwd_bs(layout=A + 3 * GB + 256) == 5
     assert fwd_bs(layout=A + 4 * GB) == 5
@@ -253,3 +256,22 @@ def test_block_sparse_validation():
     # the dK/dV kernel lists at most 8192 (query head, query block) pairs per key block
     assert bwd_bs(L=1 << 20, Hq=64, Hkv=8, P=8) == 3     # 8 x 8192 pairs
     assert bwd_bs(Hq=64, Hkv=4, P=4) == 3                # 16 query heads per K/V head
+
+
+def test_block_sparse_workspace_size():
+    ws = U.lib().ulysses_attn_bwd_block_sparse_workspace_bytes
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731  (256-byte alignment of each part)
+    for B, L, Hq, Hkv, d, P in ((1, 1024, 32, 8, 128, 8), (2, 1000, 8, 2, 64, 2), (1, 131072, 32, 32, 128, 8)):
+        Hql, Hkl = Hq // P, U.kv_local_heads(Hkv, P)
+        nb = -(-L // 128)
+        ncol = B * Hkl * nb
+        # delta, pair counts and pair lists of the layout columns (uint16, G * nb per column), plan header,
+        # work items, three tables of at most 256 split columns, 512 partial-sum slots
+        want = (r(B * Hql * L * 4) + r(Hkl * nb * 4) + r(Hkl * nb * (Hql // Hkl) * nb * 2) + r(16)
+                + r((ncol + 512) * 16) + 3 * r(256 * 4) + 512 * 2 * 128 * d * 4)
+        assert ws(B, L, Hq, Hkv, d, P, 128, 1, U.BF16) == want
+        assert ws(B, L, Hq, Hkv, d, P, 128, 0, U.BF16) == want
+    assert ws(1, 1024, 32, 8, 128, 8, 64, 1, U.BF16) == 0       # 128-token blocks only
+    assert ws(1, 1024, 32, 8, 128, 8, 128, 1, U.FP32) == 0      # bf16 only
+    assert ws(1, 1024, 64, 4, 128, 4, 128, 1, U.BF16) == 0      # 16 query heads per K/V head
+    assert ws(1, 1024, 32, 3, 128, 8, 128, 1, U.BF16) == 0      # indivisible heads

@@ -53,8 +53,8 @@ def _run(host, lay, B, L, Hq, Hkv, d, P, causal, backward=True):
     if backward:
         dq = torch.empty_like(dev["q"])
         dk, dv = torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
-        ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, L, Hq, Hkv, d, P, causal), dtype=torch.uint8,
-                         device="cuda")
+        ws = torch.empty(U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, Hq, Hkv, d, P, causal),
+                         dtype=torch.uint8, device="cuda")
         U.ulysses_attn_bwd_block_sparse(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, dq, dk, dv, layout, ws, B,
                                         L, Hq, Hkv, d, P, causal)
         out.update(dq=dq, dk=dk, dv=dv)
@@ -127,3 +127,49 @@ def test_empty_block_rows():
     check_close("dQ", dq, dq_r, "bf16")
     check_close("dK", to_f64(out["dk"], "bf16"), dk_r, "bf16")
     check_close("dV", to_f64(out["dv"], "bf16"), dv_r, "bf16")
+
+
+def test_heavy_columns_are_split_and_match():
+    """Global key blocks seen by every query block of four query heads (128
+    pairs) are cut into chunks whose partial sums are added in a fixed order:
+    the result matches the oracle and is the same on every run."""
+    B, L, Hq, Hkv, d, P, causal = 1, 4096, 8, 2, 128, 1, True
+    host, lay = _case(B, L, Hq, Hkv, d, P, causal, 2, 3, 2)
+    out = _run(host, lay, B, L, Hq, Hkv, d, P, causal)
+    again = _run(host, lay, B, L, Hq, Hkv, d, P, causal)
+    for n in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(to_host_bits(out[n]), to_host_bits(again[n]), err_msg=n)
+    f = {n: oracle.to_f64(host[n], "bf16") for n in host}
+    G = Hq // Hkv
+    kr, vr = np.repeat(f["k"], G, axis=2), np.repeat(f["v"], G, axis=2)
+    dq_r, dk_rep, dv_rep = oracle.attn_bwd_block_sparse(f["q"], kr, vr, f["do"], lay, BLOCK, causal)
+    check_close("dQ", to_f64(out["dq"], "bf16"), dq_r, "bf16")
+    for name, rep in (("dK", dk_rep), ("dV", dv_rep)):
+        parts = np.moveaxis(rep.reshape(B, L, Hkv, G, d), 3, 0)
+        want = parts.sum(axis=0)
+        check_close(name, to_f64(out[name.lower()], "bf16"), want, "bf16",
+                    allowed=shared_head_allowed(parts, want, "bf16"))
+
+
+def test_columns_beyond_the_partial_slots_stay_whole():
+    """A full bidirectional layout over 128 key blocks and 4 heads asks for 2048
+    partial-sum slots; the first 512 split the columns of head 0, the columns of
+    heads 1-3 are walked whole. Sampled key columns of both kinds, and sampled
+    query rows, match the oracle."""
+    B, L, H, d, P, causal = 1, 16384, 4, 64, 1, False
+    nb = L // BLOCK
+    host = {n: _draw(B, L, H, d, n, 913) for n in ("q", "k", "v", "do")}
+    lay = np.ones((H, nb, nb), np.uint8)
+    out = _run(host, lay, B, L, H, H, d, P, causal)
+    f = {n: oracle.to_f64(host[n], "bf16") for n in host}
+    cols = [0, 127, 5000, 16383]
+    for h in (0, 1):
+        _, dk_r, dv_r = oracle.attn_dkv_cols_block_sparse(f["q"][0, :, h], f["k"][0, :, h], f["v"][0, :, h],
+                                                          f["do"][0, :, h], cols, lay[h], BLOCK, causal)
+        check_close(f"dK head {h}", to_f64(out["dk"][0, cols, h], "bf16"), dk_r, "bf16", fro=False)
+        check_close(f"dV head {h}", to_f64(out["dv"][0, cols, h], "bf16"), dv_r, "bf16", fro=False)
+    rows = [1, 4096, 16383]
+    r = oracle.attn_rows_block_sparse(f["q"][0, :, 3], f["k"][0, :, 3], f["v"][0, :, 3], rows, lay[3], BLOCK,
+                                      causal, do=f["do"][0, :, 3])
+    check_close("O rows", to_f64(out["o"][0, rows, 3], "bf16"), r["o"], "bf16", fro=False)
+    check_close("dQ rows", to_f64(out["dq"][0, rows, 3], "bf16"), r["dq"], "bf16", fro=False)

@@ -87,8 +87,9 @@ class Run:
         else:
             U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o0["o"], self.lse, B, L, Lk, H, Hk, d, P, wl.causal)
         if wl.backward:
-            ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, wl.causal),
-                             dtype=torch.uint8, device="cuda")
+            ws_bytes = (U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, H, Hk, d, P, wl.causal) if wl.block
+                        else U.ulysses_attn_bwd_gqa_workspace_bytes(B, L, Lk, H, Hk, d, P, wl.causal))
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
             if wl.block:
                 U.ulysses_attn_bwd_block_sparse(r0["q"], r0["k"], r0["v"], o0["o"], r0["do"], self.lse, o0["dq"],
                                                 o0["dk"], o0["dv"], lay, ws, B, L, H, Hk, d, P, wl.causal)
@@ -248,8 +249,9 @@ def test_causal_prefix_matches_full_run_and_oracle(key):
         do = run.oracle_head("do")[:, :Lp]
         dq = torch.empty_like(o)
         dk, dv = torch.empty_like(r0["k"]), torch.empty_like(r0["v"])
-        ws = torch.empty(U.ulysses_attn_bwd_gqa_workspace_bytes(B, Lp, Lp, H, Hk, d, P), dtype=torch.uint8,
-                         device="cuda")
+        ws_bytes = (U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, Lp, H, Hk, d, P) if wl.block
+                    else U.ulysses_attn_bwd_gqa_workspace_bytes(B, Lp, Lp, H, Hk, d, P))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         if wl.block:
             U.ulysses_attn_bwd_block_sparse(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, lay_dev, ws, B,
                                             Lp, H, Hk, d, P, True)
