@@ -361,10 +361,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       for (int u = 0; u < 2; ++u) {
         sc[u] = f32x16{};
         dp[u] = f32x16{};
+        // all of the half's Q and dO fragments are read before its MFMAs
+        // start, so that the MFMAs do not each wait on a fresh LDS read
+        bf16x8 qa[KS], da[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          sc[u] = mfma32(frag_row<ST>(Qc, 32 * u, 16 * ks, lane), kf[ks], sc[u]);
-          dp[u] = mfma32(frag_row<ST>(Dc, 32 * u, 16 * ks, lane), vf[ks], dp[u]);
+          qa[ks] = frag_row<ST>(Qc, 32 * u, 16 * ks, lane);
+          da[ks] = frag_row<ST>(Dc, 32 * u, 16 * ks, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          sc[u] = mfma32(qa[ks], kf[ks], sc[u]);
+          dp[u] = mfma32(da[ks], vf[ks], dp[u]);
         }
       }
 #pragma unroll
@@ -560,10 +569,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        bf16x8 ka[KS], va[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32(frag_row<KST>(Kc, 32 * mt, 16 * ks, lane), qf[ks], s);
-        dp = mfma32(frag_row<VST>(Vc, 32 * mt, 16 * ks, lane), df[ks], dp);
+        for (int ks = 0; ks < KS; ++ks) {
+          ka[ks] = frag_row<KST>(Kc, 32 * mt, 16 * ks, lane);
+          va[ks] = frag_row<VST>(Vc, 32 * mt, 16 * ks, lane);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = mfma32(ka[ks], qf[ks], s);
+          dp = mfma32(va[ks], df[ks], dp);
+        }
+        // LDS reads run LOOK fragments ahead of the MFMAs that use them (the
+        // registers of this kernel leave room for 4, not for all 16; a few
+        // values live across the two tile loops go to scratch once per
+        // workgroup, outside the loops)
+        constexpr int LOOK = 4;
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS - LOOK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, LOOK, 0);
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {

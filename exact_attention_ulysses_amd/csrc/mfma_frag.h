@@ -44,6 +44,13 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 }
 
 
+// Instruction classes for __builtin_amdgcn_sched_group_barrier (LLVM AMDGPU
+// scheduling-group mask bits): a kernel lists groups in the order the
+// scheduler must emit them, e.g. LDS reads a few fragments ahead of the MFMAs
+// that consume them instead of one read, one wait, one MFMA at a time.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
