@@ -13,11 +13,12 @@
 // so every output element is written once, without atomics, and results are
 // bitwise reproducible; the price is that S and dP are formed twice.
 //
-// bf16 dK/dV kernel: workgroup = 4 waves x 32 key rows; K and V of a wave's
-//   keys stay in registers; query tiles of 64 rows (Q, dO, lse, delta) are
-//   staged through LDS. S = Q K^T and dP = dO V^T put keys across lanes, so
-//   the accumulators become the B operands of dV^T += dO^T P and
-//   dK^T += Q^T dS directly; dO^T and Q^T are read transposed from LDS.
+// bf16 dK/dV kernel: workgroup = 4 producer/consumer wave pairs x 32 key
+//   rows; K and V of a pair's keys stay in the producer's registers; query
+//   tiles of 64 rows (Q, dO, lse, delta) are staged through LDS. S = Q K^T
+//   and dP = dO V^T put keys across lanes, so the accumulators become the B
+//   operands of dV^T += dO^T P and dK^T += Q^T dS directly; dO^T and Q^T are
+//   read transposed from LDS.
 // bf16 dQ kernel: workgroup = 4 waves x 32 query rows; the forward kernel's
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
 // Grouped-query attention (pinyu.ai, section "Head-count constraints"): a key
@@ -25,6 +26,9 @@
 //   workgroup walks the query tiles of all G heads in turn and accumulates
 //   into the same registers. Keys may be fewer or more than queries
 //   (cross-attention, bidirectional only).
+// Block layouts: the same kernels visit only the active (query block, key
+//   block) pairs; heavily attended key blocks are split across workgroups
+//   whose fp32 partial sums a last kernel adds in a fixed order.
 #include <math.h>
 
 #include <type_traits>
