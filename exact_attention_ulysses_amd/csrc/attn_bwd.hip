@@ -216,7 +216,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
-    float scale, const uint8_t* __restrict__ layout, int nb, const SparsePlan plan) {
+    float scale, const uint8_t* __restrict__ layout, int nb, const SparsePlan plan, int nkb_all) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256, RSTEP = 256 / CPR;
   constexpr int ST = Stride<D>::both;  // Q and dO tiles are read along rows and transposed
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
@@ -233,8 +233,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave < 4;
   const int pw = wave & 3;                 // key group of this wave (shared by the pair)
-  // dense: key block 0 has the most query tiles under the causal mask;
-  // block layouts: the planned work item (key block column, chunk of its pairs)
+  // dense: job (key block, head pair), key block 0 having the most query
+  // tiles under the causal mask; block layouts: the planned work item (key
+  // block column, chunk of its pairs)
   int col = blockIdx.x, chunk = 0, nchunk = 1, slot = 0;
   if constexpr (SPARSE) {
     if ((int)blockIdx.x >= plan.header[0]) return;   // no work item (uniform for the workgroup)
@@ -244,8 +245,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     nchunk = it.z;
     slot = it.w;
   }
-  const int kb = SPARSE ? col % (nb) : (int)blockIdx.x / nhb;
-  const int hb = SPARSE ? col / (nb) : (int)blockIdx.x % nhb;   // (batch, key head) pair
+  if constexpr (!SPARSE) {
+    // jobs (key block kb, head pair hb) in order kb * nhb + hb, longest first.
+    // Workgroup i runs on XCD i mod 8 (round-robin dispatch); each XCD takes
+    // runs of 32 consecutive jobs, so that the workgroups sharing its L2 walk
+    // neighbouring key blocks, which read the same query tiles a few steps
+    // apart. Runs go to XCDs 0..7 and 7..0 in alternate rounds of 256 jobs,
+    // which keeps the causal work of the XCDs even.
+    const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+    const int round = j >> 5;
+    col = 256 * round + 32 * ((round & 1) ? 7 - x : x) + (j & 31);
+    if (col >= nkb_all * nhb) return;   // grid rounded up to whole rounds
+  }
+  const int kb = SPARSE ? col % (nb) : col / nhb;
+  const int hb = SPARSE ? col / (nb) : col % nhb;   // (batch, key head) pair
   const int b = hb / Hk, hk = hb - b * Hk;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;   // row strides
   // query heads hk*G .. hk*G + G-1 share this key head; g selects one of them
@@ -855,14 +868,16 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
     hipLaunchKernelGGL(bwd_sparse_plan_kernel, dim3(1), dim3(256), 0, stream, ncol, nlcol, plan);
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)(ncol + kSparseSlots)), dim3(512), 0,
                        stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb, plan);
+                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb, plan,
+                       nkb);
     hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D>), dim3(1024), dim3(256), 0, stream, plan, nb, s.Lk, s.Hk,
                        (__bf16*)dk, (__bf16*)dv, scale);
   } else {
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nkb * nkhb), dim3(512), 0, stream,
+    const unsigned grid = (unsigned)((nkb * nkhb + 255) / 256 * 256);   // whole rounds of 256 jobs
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0,
-                       SparsePlan{});
+                       SparsePlan{}, nkb);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
