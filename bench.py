@@ -148,6 +148,17 @@ def parse():
     return ap.parse_args()
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, seq_host, tokens: int, layout=None):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload."""
     import numpy as np
@@ -188,7 +199,7 @@ def cpu_baseline(wl, seq_host, tokens: int, layout=None):
         flops = 4 * d * npairs(Ls, wl.causal, Lks)
     t_attn = time.perf_counter() - t0
     return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": threads if threads else cores,
-            "host_cores_visible": cores, "kind": "oracle",
+            "host_cores_visible": cores, "cpu_model": _cpu_model(), "kind": "oracle",
             "sample": (f"fp64 numpy oracle, {'fwd+bwd' if wl.backward else 'fwd'} of head 0 of rank 0 over the "
                        f"first {Ls} query and {Lks} key tokens of the same inputs ({t_attn:.1f} s); flops "
                        f"counted as on the GPU"),

@@ -22,6 +22,9 @@
 //   key/value buffers may hold fewer heads than the query buffer; query head h
 //   reads key head h / G. Queries and keys may have different lengths
 //   (cross-attention, papers.chlience.com note, section 5.4; bidirectional only).
+// Block layouts (paper-graph summary, section 3.4 and Figs 6-7, "blocked
+//   sparse attention"): a workgroup visits only the key blocks its query
+//   block's layout row marks, found with a 64-lane ballot over the row.
 // fp32 path: one lane per query row, K/V tiles in LDS, plain FMAs (used for
 //   the small fp32 workloads; precision reference for the tests).
 #include <math.h>

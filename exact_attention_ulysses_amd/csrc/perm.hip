@@ -13,8 +13,9 @@
 // kernel therefore copies 16-byte words straight from HBM to HBM: a wave's
 // 64 lanes move 1 KiB of consecutive seq-layout words, which on the
 // head-layout side form runs of at least 128 contiguous bytes, so every line
-// read and written is a full line. Staging through LDS would add a round trip without making any access
-// wider. Values are never converted; bits are copied as they are. Both
+// read and written is a full line. Staging through LDS would add a round
+// trip without making any access wider. Values are never converted; bits are
+// copied as they are. Both
 // directions walk the seq-layout tensor in order (seq_to_head reads it,
 // head_to_seq writes it), so the runs are always on the head-layout side.
 //
