@@ -304,6 +304,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsq + scol) * 2);
   u32x4 qreg[CH], dreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
+  bool row_ok = false;
   // Step t handles the query tile starting at row q0 of the group's query head
   // g: dense, tile t mod nqt of head t div nqt; with a block layout, half t & 1
   // of the listed pair t / 2. `diag` marks the tiles that reach above a key of
@@ -334,12 +335,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       dreg[j] = buf_load16(drs, voff[j] + soff, 0);
     }
     if (tid < BQ) {
+      // raw values only: they are first used when the tile is stored, a step
+      // later, so this wave does not wait here for the loads (rows past the
+      // end read the last row and are fixed up at the store)
       const int qi = q0 + tid;
-      // rows past the end, and rows that see no key (LSE -inf, block layouts
-      // only), get lse = +inf, so their probabilities are exactly 0
-      const float l = qi < Lq ? lseh[(size_t)g * Lq + qi] : INFINITY;
-      lse_r = l == -INFINITY ? INFINITY : l * kLog2e;
-      dl_r = qi < Lq ? dlh[(size_t)g * Lq + qi] : 0.f;
+      row_ok = qi < Lq;
+      const size_t qc = (size_t)g * Lq + (row_ok ? qi : Lq - 1);
+      lse_r = lseh[qc];
+      dl_r = dlh[qc];
     }
   };
   auto store_tile = [&](int buf) {
@@ -349,8 +352,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       *reinterpret_cast<u32x4*>(&Ds[buf][(srow + j * RSTEP) * ST + scol]) = dreg[j];
     }
     if (tid < BQ) {
-      lse2s[buf][tid] = lse_r;
-      dls[buf][tid] = dl_r;
+      // rows past the end, and rows that see no key (LSE -inf, block layouts
+      // only), get lse = +inf, so their probabilities are exactly 0
+      lse2s[buf][tid] = (!row_ok || lse_r == -INFINITY) ? INFINITY : lse_r * kLog2e;
+      dls[buf][tid] = row_ok ? dl_r : 0.f;
     }
   };
 
