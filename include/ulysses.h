@@ -16,9 +16,10 @@
  *    sqrt(d_h)) V'_p on rank p's head group; section 5.4: cross-attention
  *    among the attention kinds the method carries.
  *  - pinyu.ai, "Head-count constraints", and the aifetchly blog, "Practical
- *    Deployment Checklist for Long-Context Training": grouped-query / multi-query attention has fewer K/V heads than
- *    query heads; they split over P ranks when H_kv % P == 0, and otherwise
- *    each rank holds a replica of the K/V head its query heads use.
+ *    Deployment Checklist for Long-Context Training": grouped-query /
+ *    multi-query attention has fewer K/V heads than query heads; they split
+ *    over P ranks when H_kv % P == 0, and otherwise each rank holds a replica
+ *    of the K/V head its query heads use.
  *
  * Conventions shared by every entry point
  *  - Element types: ULYSSES_BF16 (bfloat16) or ULYSSES_FP32. The layout

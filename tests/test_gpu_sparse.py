@@ -129,11 +129,13 @@ def test_empty_block_rows():
     check_close("dV", to_f64(out["dv"], "bf16"), dv_r, "bf16")
 
 
-def test_heavy_columns_are_split_and_match():
-    """Global key blocks seen by every query block of four query heads (128
-    pairs) are cut into chunks whose partial sums are added in a fixed order:
-    the result matches the oracle and is the same on every run."""
-    B, L, Hq, Hkv, d, P, causal = 1, 4096, 8, 2, 128, 1, True
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,causal", [(1, 4096, 8, 2, 128, True), (2, 2048, 4, 1, 64, False)])
+def test_heavy_columns_are_split_and_match(B, L, Hq, Hkv, d, causal):
+    """Global key blocks seen by every query block of four query heads (64 to
+    128 pairs) are cut into chunks whose partial sums are added in a fixed
+    order: the result matches the oracle and is the same on every run (the
+    second case splits columns of both batch entries)."""
+    P = 1
     host, lay = _case(B, L, Hq, Hkv, d, P, causal, 2, 3, 2)
     out = _run(host, lay, B, L, Hq, Hkv, d, P, causal)
     again = _run(host, lay, B, L, Hq, Hkv, d, P, causal)
