@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan,
 // dK^T += Q^T dS. Neither role needs more than 256 registers, so the pair
 // shares a SIMD and the producer's exponentials and products run while the
 // consumer's MFMAs do. Tiles are double buffered; each step ends with two
-// barriers (hand-over, then the staging of the next tile).
+// barriers (hand-over, then the staging of the next tile, which producers
+// (dO) and consumers (Q) share).
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -291,18 +292,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     __syncthreads();
   }
 
-  // staging of Q, dO, lse, delta by the producer waves (threads 0..255) through
-  // buffer loads; rows past the end of the sequence read as zero (the range
-  // covers Lq rows from the group's first head, and every head of the group
-  // lies inside a row)
-  const int srow = tid / CPR, scol = (tid % CPR) * 8;
+  // staging of the query tiles through buffer loads, split between the roles
+  // so that each wave moves half as much while the workgroup waits between
+  // its two barriers: the producers stage dO (and the LSE / delta rows), the
+  // consumers Q; each role's 256 threads cover one 64 x D tile. Rows past the
+  // end of the sequence read as zero (the range covers Lq rows from the
+  // group's first head, and every head of the group lies inside a row).
+  const int stid = tid & 255;
+  const int srow = stid / CPR, scol = (stid % CPR) * 8;
   const uint32_t head_bytes = (uint32_t)((size_t)Lq * rsq * 2);
-  const __amdgpu_buffer_rsrc_t qrs = head_rsrc(qh, head_bytes);
-  const __amdgpu_buffer_rsrc_t drs = head_rsrc(doh, head_bytes);
+  const __amdgpu_buffer_rsrc_t srs = head_rsrc(producer ? doh : qh, head_bytes);
   uint32_t voff[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsq + scol) * 2);
-  u32x4 qreg[CH], dreg[CH];
+  u32x4 sreg[CH];
   float lse_r = 0.f, dl_r = 0.f;
   bool row_ok = false;
   // Step t handles the query tile starting at row q0 of the group's query head
@@ -330,10 +333,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     tile_of(t, g, q0, diag);
     const uint32_t soff = (uint32_t)q0 * (uint32_t)(rsq * 2) + (uint32_t)(g * D * 2);
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      qreg[j] = buf_load16(qrs, voff[j] + soff, 0);
-      dreg[j] = buf_load16(drs, voff[j] + soff, 0);
-    }
+    for (int j = 0; j < CH; ++j) sreg[j] = buf_load16(srs, voff[j] + soff, 0);
     if (tid < BQ) {
       // raw values only: they are first used when the tile is stored, a step
       // later, so this wave does not wait here for the loads (rows past the
@@ -346,11 +346,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     }
   };
   auto store_tile = [&](int buf) {
+    __bf16* dst = producer ? Ds[buf] : Qs[buf];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      *reinterpret_cast<u32x4*>(&Qs[buf][(srow + j * RSTEP) * ST + scol]) = qreg[j];
-      *reinterpret_cast<u32x4*>(&Ds[buf][(srow + j * RSTEP) * ST + scol]) = dreg[j];
-    }
+    for (int j = 0; j < CH; ++j) *reinterpret_cast<u32x4*>(&dst[(srow + j * RSTEP) * ST + scol]) = sreg[j];
     if (tid < BQ) {
       // rows past the end, and rows that see no key (LSE -inf, block layouts
       // only), get lse = +inf, so their probabilities are exactly 0
@@ -358,6 +356,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       dls[buf][tid] = row_ok ? dl_r : 0.f;
     }
   };
+
+  // both roles stage their half of tile 0 and load their half of tile 1
+  if (nsteps > 0) load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  if (nsteps > 1) load_tile(1);
 
   if (producer) {
     // ---------------- producer: S, dP, P, dS ----------------
@@ -425,10 +429,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
         }
       }
     };
-    if (nsteps > 0) load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    if (nsteps > 1) load_tile(1);
     for (int s = 0; s <= nsteps; ++s) {
       if (s < nsteps) {
         int g, q0;
@@ -452,7 +452,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       dkacc[dt] = f32x16{};
       dvacc[dt] = f32x16{};
     }
-    __syncthreads();  // tile 0 staged
     for (int s = 0; s <= nsteps; ++s) {
       if (s >= 1) {
         const int prev = (s - 1) & 1;
@@ -469,7 +468,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
           }
         }
       }
-      __syncthreads();
+      __syncthreads();  // consumers are done with tile s-1's buffers
+      if (s + 1 < nsteps) store_tile((s + 1) & 1);
+      if (s + 2 < nsteps) load_tile(s + 2);
       __syncthreads();
     }
     if (SPARSE && nchunk > 1) {
