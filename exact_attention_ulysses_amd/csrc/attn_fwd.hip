@@ -8,23 +8,28 @@
 // maximum and row sum, and writes the log-sum-exp of every row for the
 // backward pass.
 //
-// bf16 path (gfx950 MFMA, 32x32x16):
-//   workgroup = 4 waves x 32 query rows = 128 rows; key blocks of 64 rows.
-//   Each wave computes S^T = K Q^T for its rows (keys down the accumulator
-//   rows, queries across lanes), so a query's scores sit in one lane pair and
-//   the row max / sum need one cross-lane exchange. O^T = V^T P^T reuses the
-//   score registers as the B operand; V is read transposed from its row-major
-//   LDS tile with ds_read_b64_tr_b16. Q stays in registers for the whole key
-//   walk; the next K/V tile is loaded into registers while the current one is
-//   used from LDS. Causal query blocks are dispatched longest first and never
-//   visit key blocks above the diagonal.
+// bf16 path (gfx950 MFMA, 32x32x16), key tiles of 64 rows:
+//   each wave owns 32 query rows and computes S^T = K Q^T for them (keys down
+//   the accumulator rows, queries across lanes), so a query's scores sit in
+//   one lane pair and the row max / sum need one cross-lane exchange.
+//   O^T = V^T P^T reuses the score registers as the B operand; V is read
+//   transposed from its row-major LDS tile with ds_read_b64_tr_b16. Q stays
+//   in registers for the whole key walk; the next K/V tile is loaded into
+//   registers while the current one is used from LDS. Causal query blocks are
+//   dispatched longest first and never visit key blocks above the diagonal.
+//   Dense attention: 8 waves x 32 rows = 256 rows per workgroup in two groups
+//   whose MFMA and softmax phases alternate (attn_fwd_bf16_kernel). Block
+//   layouts: 4 waves x 32 rows = 128 rows, the layout's block, walking the
+//   active key blocks (attn_fwd_sparse_bf16_kernel). Both compute every row
+//   with the same sequence of operations, so a full layout gives the dense
+//   result bit for bit.
 // Grouped-query attention (pinyu.ai, section "Head-count constraints"): the
 //   key/value buffers may hold fewer heads than the query buffer; query head h
 //   reads key head h / G. Queries and keys may have different lengths
 //   (cross-attention, papers.chlience.com note, section 5.4; bidirectional only).
 // Block layouts (paper-graph summary, section 3.4 and Figs 6-7, "blocked
-//   sparse attention"): a workgroup visits only the key blocks its query
-//   block's layout row marks, found with a 64-lane ballot over the row.
+//   sparse attention"): the workgroup of a query block visits only the key
+//   blocks its layout row marks, found with a 64-lane ballot over the row.
 // fp32 path: one lane per query row, K/V tiles in LDS, plain FMAs (used for
 //   the small fp32 workloads; precision reference for the tests).
 #include <math.h>
@@ -43,8 +48,10 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+// Block layouts: workgroup = 4 waves x 32 query rows, one 128-row query block;
+// it walks the active key blocks of the block's layout row.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fwd_sparse_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
     float sl2, const uint8_t* __restrict__ layout, int nb) {
@@ -89,9 +96,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   // running maximum in log2 units and this lane's share of the running sum
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
-  const int nkb = (kend + BN - 1) / BN;
-
   // staging: thread tid moves chunks of rows srow + j * RSTEP, columns scol .. scol+7,
   // through buffer loads (constant per-lane offset, scalar tile offset)
   const int srow = tid / CPR, scol = (tid % CPR) * 8;
@@ -121,10 +125,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
 
   // One key tile kb, held in LDS buffer cur; afterwards the tile in the
   // staging registers goes to the other buffer (if store) and key tile `next2`
-  // is loaded into the registers (if >= 0). EDGE tiles cross the diagonal (or
-  // the end of the keys) and need the mask; the steady-state loop runs without it.
-  auto tile = [&](int cur, int kb, bool store, int next2, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
+  // is loaded into the registers (if >= 0). The mask applies only where the
+  // tile crosses the diagonal or the end of the keys.
+  auto tile = [&](int cur, int kb, bool store, int next2) {
     const __bf16* Kc = Ks[cur];
     const __bf16* Vc = Vs[cur];
     const int k0 = kb * BN;
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
     }
 
-    if (EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk))) {
+    if (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk)) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       m_run = m2;
     }
     // (a block-sparse row may meet a fully masked tile before any visible key)
-    const float nm = (SPARSE && m_run == -INFINITY) ? 0.f : -m_run;
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
     float rsum = 0.f;
     bf16x8 pf[4];
 #pragma unroll
@@ -189,21 +192,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
     if (next2 >= 0) load_tile(next2);
     __syncthreads();
   };
-  const auto steady = std::integral_constant<bool, false>{};
-  const auto edge = std::integral_constant<bool, true>{};
-
-  if constexpr (!SPARSE) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    if (nkb > 1) load_tile(1);
-    // causal: only the last two key tiles reach above a query row of this block;
-    // otherwise only a ragged last tile holds keys past the end
-    const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
-    int kb = 0;
-    for (; kb < nsteady; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, steady);
-    for (; kb < nkb; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, edge);
-  } else {
+  {
     // The active key blocks j of this query block (ascending; causal: j <= qb),
     // two key tiles each: tile (j, half) sits in LDS buffer `half`. A second
     // tile past the end of the keys is fully masked (its loads read zeros).
@@ -221,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
       int half = 0;
       while (j >= 0) {
         // next tile: (j, 1) or (jn, 0); the one after: (jn, half)
-        tile(half, 2 * j + half, half == 0 || jn >= 0, jn >= 0 ? 2 * jn + half : -1, edge);
+        tile(half, 2 * j + half, half == 0 || jn >= 0, jn >= 0 ? 2 * jn + half : -1);
         if (half == 1) {
           j = jn;
           if (j >= 0) jn = scan.next(lane);
@@ -232,6 +221,195 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   }
 
   // a row that sees no key (possible only under a block layout) has zero output and LSE -inf
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < Lq) {
+    __bf16* orow = o + qoff + (size_t)qrow * rsq;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
+    }
+    if (hl == 0) lse[(size_t)hb * Lq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// Dense bf16 forward as a ping-pong of two wave groups. A workgroup has 8
+// waves and 256 query rows: group A = waves 0-3, group B = waves 4-7; wave
+// (group g, index w) owns rows q0 + 64 w + 32 g .. +31, so both groups span
+// the block alike. With the usual in-order placement each SIMD hosts one wave
+// of each group. The groups alternate phases separated by barriers: while one
+// runs its MFMA phase for key tile k (O^T += V^T P^T of tile k, then the
+// scores of tile k+1), the other runs its softmax phase (mask, row max,
+// exponentials, row sums, P to bf16) and stages the next tile, so every SIMD
+// has MFMA work from one wave and VALU work from the other at all times.
+// Group A stages K tiles (K(k+1) during its softmax of tile k), group B stages
+// V tiles (V(k+1) during its softmax of tile k); each LDS buffer is free by
+// the time it is written (K(k+1) replaces K(k-1), last read by B's scores of
+// tile k-1 one phase earlier; likewise for V).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
+    float sl2) {
+  constexpr int BM = 256, BN = 64, KS = D / 16, DT = D / 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int CH = BN * CPR / 256;         // chunks per thread of its group's tile
+  constexpr int RSTEP = 256 / CPR;           // rows between a thread's chunks
+  constexpr int KST = Stride<D>::row;
+  constexpr int VST = Stride<D>::col;
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KST];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool groupA = wave < 4;
+  const int gtid = tid & 255;                // thread index within the group
+  const int bid = blockIdx.x;
+  const int qb = nqb - 1 - bid / nhb;        // longest rows first
+  const int hb = bid % nhb;
+  const int b = hb / Hq, h = hb - b * Hq;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
+  const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
+  const __bf16* qh = q + qoff;
+  const int q0 = qb * BM;
+  const int qw0 = q0 + 64 * (wave & 3) + 32 * (wave >> 2);
+  const int qrow = qw0 + l32;
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qrow < Lq)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * rsq + 16 * ks + 8 * hl);
+    else
+      qf[ks] = bf16x8{};
+  }
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
+  const int n = (kend + BN - 1) / BN;
+  // causal: the last BM / BN key tiles reach above some row of the block;
+  // otherwise only a ragged last tile holds keys past the end
+  const int nsteady = CAUSAL ? max(0, n - BM / BN) : (Lk % BN ? n - 1 : n);
+
+  // staging: group A moves K tiles, group B V tiles; thread gtid handles
+  // chunks of rows srow + j * RSTEP, columns scol .. scol + 7
+  const int srow = gtid / CPR, scol = (gtid % CPR) * 8;
+  const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
+  const __amdgpu_buffer_rsrc_t rsrc = head_rsrc((groupA ? k : v) + koff, head_bytes);
+  uint32_t voff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsk + scol) * 2);
+  const uint32_t tile_bytes = (uint32_t)(BN * rsk * 2);
+  u32x4 sreg[CH];
+  auto load = [&](int kb) {
+    const uint32_t soff = (uint32_t)kb * tile_bytes;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) sreg[j] = buf_load16(rsrc, voff[j] + soff, 0);
+  };
+  auto store = [&](int buf) {
+    __bf16* t = groupA ? Ks[buf] : Vs[buf];
+    const int st = groupA ? KST : VST;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) *reinterpret_cast<u32x4*>(&t[(srow + j * RSTEP) * st + scol]) = sreg[j];
+  };
+
+  f32x16 s0, s1;        // scores of the current tile
+  bf16x8 pf[4];         // its probabilities as MFMA operands
+  auto scores = [&](int kb) {
+    const __bf16* Kc = Ks[kb & 1];
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma32(frag_row<KST>(Kc, 0, 16 * ks, lane), qf[ks], s0);
+      s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
+    }
+  };
+  auto pv = [&](int kb) {
+    const __bf16* Vc = Vs[kb & 1];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<VST>(Vc, 16 * c, 32 * dt, lane), pf[c], oacc[dt]);
+    }
+  };
+  auto softmax = [&](int kb) {
+    const int k0 = kb * BN;
+    if (kb >= nsteady && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk))) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (CAUSAL ? (key > qrow) : (key >= Lk)) s0[e] = -INFINITY;
+        if (CAUSAL ? (key + 32 > qrow) : (key + 32 >= Lk)) s1[e] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mcand = mx * sl2;
+    // lazy rescale, as in the four-wave kernel
+    if (__ballot(mcand > m_run + 8.f)) {
+      const float m2 = fmaxf(m_run, mcand);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_run = m2;
+    }
+    const float nm = -m_run;
+    float rsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = (c < 2) ? s0[8 * (c & 1) + i] : s1[8 * (c & 1) + i];
+        const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, nm));
+        rsum += p;
+        pf[c][i] = (__bf16)p;
+      }
+    }
+    l_run += rsum;
+  };
+
+  // prologue: K(0) and V(0) into LDS, K(1) / V(1) in flight; group A forms
+  // the scores of tile 0 while group B waits
+  load(0);
+  store(0);
+  if (n > 1) load(1);
+  __syncthreads();
+  if (groupA) scores(0);
+  __syncthreads();
+
+  if (groupA) {
+    for (int kb = 0; kb < n; ++kb) {
+      softmax(kb);
+      if (kb + 1 < n) store((kb + 1) & 1);   // K(kb+1)
+      if (kb + 2 < n) load(kb + 2);
+      __syncthreads();
+      pv(kb);
+      if (kb + 1 < n) scores(kb + 1);
+      __syncthreads();
+    }
+  } else {
+    for (int kb = 0; kb < n; ++kb) {
+      if (kb >= 1) pv(kb - 1);
+      scores(kb);
+      __syncthreads();
+      softmax(kb);
+      if (kb + 1 < n) store((kb + 1) & 1);   // V(kb+1)
+      if (kb + 2 < n) load(kb + 2);
+      __syncthreads();
+    }
+    pv(n - 1);
+  }
+
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < Lq) {
@@ -316,13 +494,15 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   const float sl2 = kLog2e / sqrtf((float)D);
   const int nb = (s.Lk + kSparseBlock - 1) / kSparseBlock;
   if (s.layout)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+    hipLaunchKernelGGL((attn_fwd_sparse_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
                        s.Hk, s.Hq / s.Hk, nqb, nhb, sl2, s.layout, nb);
-  else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+  else {
+    const int nqb2 = (s.Lq + 255) / 256;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb2 * nhb), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
-                       s.Hk, s.Hq / s.Hk, nqb, nhb, sl2, nullptr, 0);
+                       s.Hk, s.Hq / s.Hk, nqb2, nhb, sl2);
+  }
   return hipGetLastError();
 }
 
