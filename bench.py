@@ -14,6 +14,7 @@ the whole step time (transposes included); per-op figures come from HIP
 events recorded on the launch stream around every call in the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --gemm-ceiling      # vendor bf16 GEMM rate, for context
 
 HBM traffic of the dominant op (roofline "traffic"): two rocprofv3 counter
 runs of this script with --calibration-copy, one collecting FETCH_SIZE and
@@ -143,6 +144,8 @@ def parse():
                     help="prefix length of one head that the fp64 oracle runs fwd+bwd on")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 runs)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time the vendor bf16 GEMM (torch.matmul) on random and constant operands instead")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CMD_FETCH", "CMD_WRITE"),
                     help="reduce two rocprofv3 counter runs to profiles/hbm_traffic_<workload>.json")
     return ap.parse_args()
@@ -207,15 +210,54 @@ def cpu_baseline(wl, seq_host, tokens: int, layout=None):
             "perm_sample": f"seq_to_head of rank 0's share of {len(seq_host)} tensors ({t_perm:.1f} s)"}
 
 
+def gemm_ceiling() -> None:
+    """bf16 GEMM rate of the vendor library (torch.matmul -> hipBLASLt) on seeded
+    N(0,1) operands and on all-ones operands: a practical MFMA ceiling for this
+    chip under its power limit (random bits toggle more and lower the clock),
+    printed as one JSON line beside the published dense peak."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    res = []
+    for n in (8192, 16384):
+        for kind in ("randn", "ones"):
+            if kind == "randn":
+                a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+                b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+            else:
+                a = torch.ones((n, n), device=dev, dtype=torch.bfloat16)
+                b = torch.ones((n, n), device=dev, dtype=torch.bfloat16)
+            c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+            for _ in range(3):
+                torch.matmul(a, b, out=c)
+            torch.cuda.synchronize()
+            reps = 20 if n == 8192 else 5
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(a, b, out=c)
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res.append({"m_n_k": n, "operands": kind, "ms": ms, "TFLOPs": 2 * n ** 3 / ms / 1e9,
+                        "frac_peak": 2 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS})
+            del a, b, c
+    print(json.dumps({"gemm_ceiling": res, "peak_TFLOPs": PEAK_BF16_TFLOPS, "dtype": "bf16"}))
+
+
 def main():
     args = parse()
+    if args.gemm_ceiling:
+        gemm_ceiling()
+        return
     if args.summarize_traffic:
         from workloads import HEADLINE
         summarize_traffic(args.workload or HEADLINE, *args.summarize_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU exchange is not "
-              "part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the exchange between GPUs is not "
+              "implemented", file=sys.stderr)
         sys.exit(2)
     import torch
 
