@@ -359,6 +359,26 @@ def test_backward_invariants_and_closed_forms():
     assert not dqz.any() and not dkz.any() and not dvz.any()
 
 
+@pytest.mark.parametrize("Lq,Lk,causal", [(300, 300, True), (70, 70, False), (45, 300, False)])
+def test_zero_query_closed_forms(Lq, Lk, causal):
+    """With Q = 0 the oracle's O, LSE, dQ, dK and dV equal the closed forms of
+    tests/closed_forms.py, derived from uniform weights 1/n_i (dQ through the
+    running sums of v_j k_j^T and k_j, a route the oracle never takes)."""
+    from closed_forms import zero_query_attention
+    Hh, d = 2, 16
+    k, v = (_rand((1, Lk, Hh, d), s) for s in (41, 42))
+    do = _rand((1, Lq, Hh, d), 43)
+    for h in range(Hh):
+        dq, dk, dv, o, lse, _ = oracle.attn_bwd_head(np.zeros((Lq, d)), k[0, :, h], v[0, :, h], do[0, :, h],
+                                                     causal, row_block=64)
+        r = zero_query_attention(k[0, :, h], v[0, :, h], do[0, :, h], causal, Lq, block=128)
+        np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+        np.testing.assert_allclose(o, r["o"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(lse, r["lse"], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(dq, r["dq"], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, r["dv"], rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # sampled evaluation agrees with the full oracle
 # ---------------------------------------------------------------------------
