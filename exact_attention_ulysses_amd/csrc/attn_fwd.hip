@@ -18,11 +18,14 @@
 //   registers while the current one is used from LDS. Causal query blocks are
 //   dispatched longest first and never visit key blocks above the diagonal.
 //   Dense attention: 8 waves x 32 rows = 256 rows per workgroup in two groups
-//   whose MFMA and softmax phases alternate (attn_fwd_bf16_kernel). Block
-//   layouts: 4 waves x 32 rows = 128 rows, the layout's block, walking the
-//   active key blocks (attn_fwd_sparse_bf16_kernel). Both compute every row
-//   with the same sequence of operations, so a full layout gives the dense
-//   result bit for bit.
+//   whose MFMA and softmax phases alternate (attn_fwd_bf16_kernel); launches
+//   of only a few hundred query blocks instead split each 128-row block's key
+//   walk between two wave groups and merge the halves through LDS
+//   (attn_fwd_split_bf16_kernel). Block layouts: 4 waves x 32 rows = 128
+//   rows, the layout's block, walking the active key blocks
+//   (attn_fwd_sparse_bf16_kernel). The single-walk kernels compute every row
+//   with the same sequence of operations, so a full layout gives their result
+//   bit for bit.
 // Grouped-query attention (pinyu.ai, section "Head-count constraints"): the
 //   key/value buffers may hold fewer heads than the query buffer; query head h
 //   reads key head h / G. Queries and keys may have different lengths
@@ -232,6 +235,216 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_sparse_bf16_kernel(
         *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
     }
     if (hl == 0) lse[(size_t)hb * Lq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// Dense bf16 forward for grids too small to fill the chip: a workgroup of 8
+// waves owns 128 query rows and splits their key walk in two. Waves w and
+// w + 4 own the same 32 rows; group 0 (waves 0-3) takes the first half of the
+// key tiles, group 1 (waves 4-7) the second half, each through its own
+// double-buffered K/V tiles in LDS, and at the end group 0 folds group 1's
+// running maximum, sum and O accumulators into its own through LDS. The
+// longest query block's chain of key tiles is half as long as in the
+// single-walk kernels, which is what bounds a causal launch of a few hundred
+// query blocks.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
+    float sl2) {
+  constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int CH = BN * CPR / 256;         // chunks per thread of its group's tile
+  constexpr int RSTEP = 256 / CPR;           // rows between a thread's chunks
+  constexpr int KST = Stride<D>::row;
+  constexpr int VST = Stride<D>::col;
+  constexpr int KBYTES = 2 * 2 * BN * KST * 2, VBYTES = 2 * 2 * BN * VST * 2;
+  // [group][buffer] K and V tiles; reused for the merge once the walks are done
+  __shared__ __attribute__((aligned(16))) char smem[KBYTES + VBYTES];
+  typedef __bf16 KTile[BN * KST];
+  typedef __bf16 VTile[BN * VST];
+  KTile* Ks = reinterpret_cast<KTile*>(smem);
+  VTile* Vs = reinterpret_cast<VTile*>(smem + KBYTES);
+  // merge record of one wave of group 1: DT * 16 O values, the running
+  // maximum and the partial sum, each as [value][lane]
+  constexpr int MREC = (DT * 16 + 2) * 64;
+  static_assert(4 * MREC * 4 <= KBYTES + VBYTES, "merge records exceed the tile buffers");
+  float* mbuf = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wq = wave & 3;
+  const int gtid = tid & 255;                // thread index within the group
+  const int bid = blockIdx.x;
+  const int qb = nqb - 1 - bid / nhb;        // longest rows first
+  const int hb = bid % nhb;
+  const int b = hb / Hq, h = hb - b * Hq;
+  const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
+  const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
+  const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
+  const __bf16* qh = q + qoff;
+  const int q0 = qb * BM;
+  const int qw0 = q0 + 32 * wq;
+  const int qrow = qw0 + l32;
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qrow < Lq)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qh + (size_t)qrow * rsq + 16 * ks + 8 * hl);
+    else
+      qf[ks] = bf16x8{};
+  }
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // key tiles [0, n): group 0 walks [0, n / 2), group 1 [n / 2, n) -- the
+  // diagonal tiles under the causal mask, and one tile more when n is odd
+  const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
+  const int n = (kend + BN - 1) / BN;
+  const int half = n / 2;
+  const int t0 = grp ? half : 0;
+  const int cnt = grp ? n - half : half;
+  const int steps = n - half;                // both groups pass this many barriers
+
+  const int srow = gtid / CPR, scol = (gtid % CPR) * 8;
+  const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
+  const __amdgpu_buffer_rsrc_t krs = head_rsrc(k + koff, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = head_rsrc(v + koff, head_bytes);
+  uint32_t voff[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) voff[j] = (uint32_t)(((srow + j * RSTEP) * rsk + scol) * 2);
+  const uint32_t tile_bytes = (uint32_t)(BN * rsk * 2);
+  u32x4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int kb) {
+    const uint32_t soff = (uint32_t)kb * tile_bytes;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      kreg[j] = buf_load16(krs, voff[j] + soff, 0);
+      vreg[j] = buf_load16(vrs, voff[j] + soff, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* kt = Ks[2 * grp + buf];
+    __bf16* vt = Vs[2 * grp + buf];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      *reinterpret_cast<u32x4*>(&kt[(srow + j * RSTEP) * KST + scol]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&vt[(srow + j * RSTEP) * VST + scol]) = vreg[j];
+    }
+  };
+
+  // one key tile of this group, as in the four-wave kernel
+  auto tile = [&](int cur, int kb, bool store, int next2) {
+    const __bf16* Kc = Ks[2 * grp + cur];
+    const __bf16* Vc = Vs[2 * grp + cur];
+    const int k0 = kb * BN;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma32(frag_row<KST>(Kc, 0, 16 * ks, lane), qf[ks], s0);
+      s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
+    }
+    if (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk)) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
+        if (CAUSAL ? (key > qrow) : (key >= Lk)) s0[e] = -INFINITY;
+        if (CAUSAL ? (key + 32 > qrow) : (key + 32 >= Lk)) s1[e] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mcand = mx * sl2;
+    if (__ballot(mcand > m_run + 8.f)) {
+      const float m2 = fmaxf(m_run, mcand);
+      // (a lane whose rows have seen only masked keys keeps its empty state)
+      const float alpha = m2 == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m2);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_run = m2;
+    }
+    // group 1's rows of the first query tiles meet only masked keys in a
+    // diagonal tile before any visible one
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+    float rsum = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = (c < 2) ? s0[8 * (c & 1) + i] : s1[8 * (c & 1) + i];
+        const float p = __builtin_amdgcn_exp2f(fmaf(x, sl2, nm));
+        rsum += p;
+        pf[c][i] = (__bf16)p;
+      }
+    }
+    l_run += rsum;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<VST>(Vc, 16 * c, 32 * dt, lane), pf[c], oacc[dt]);
+    }
+    if (store) store_tile(cur ^ 1);
+    if (next2 >= 0) load_tile(next2);
+    __syncthreads();
+  };
+
+  if (cnt > 0) {
+    load_tile(t0);
+    store_tile(0);
+  }
+  __syncthreads();
+  if (cnt > 1) load_tile(t0 + 1);
+  for (int st = 0; st < steps; ++st) {
+    if (st < cnt)
+      tile(st & 1, t0 + st, st + 1 < cnt, st + 2 < cnt ? t0 + st + 2 : -1);
+    else
+      __syncthreads();   // group 0's idle step when n is odd
+  }
+
+  // every tile read ended at the last barrier: group 1 leaves its state in
+  // the tile buffers, group 0 folds it into its own
+  float* rec = mbuf + wq * MREC;
+  if (grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rec[(dt * 16 + e) * 64 + lane] = oacc[dt][e];
+    }
+    rec[DT * 16 * 64 + lane] = m_run;
+    rec[(DT * 16 + 1) * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  const float m1 = rec[DT * 16 * 64 + lane];
+  const float l1 = rec[(DT * 16 + 1) * 64 + lane];
+  const float m = fmaxf(m_run, m1);
+  const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+  const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = oacc[dt][e] * a0 + rec[(dt * 16 + e) * 64 + lane] * a1;
+  }
+  l_run = l_run * a0 + l1 * a1;
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < Lq) {
+    __bf16* orow = o + qoff + (size_t)qrow * rsq;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
+    }
+    if (hl == 0) lse[(size_t)hb * Lq + qrow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -486,6 +699,15 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
   }
 }
 
+// Dense launches with few 256-row query blocks W (over all batch entries and
+// heads) split each block's key walk between two wave groups. Causal: below
+// ~512 blocks the longest walk, not the total work, sets the kernel time
+// (measured at W = 256: +20-33 %; at W = 512 the single walk is 15 % faster).
+// Bidirectional walks are all equally long: splitting pays when the doubled
+// workgroup count still fits the 256 CUs at once (W = 128: +50 %).
+constexpr int64_t kSplitCausalBelow = 384;
+constexpr int64_t kSplitFullUpTo = 128;
+
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnShape& s,
                     hipStream_t stream) {
@@ -499,9 +721,15 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
                        s.Hk, s.Hq / s.Hk, nqb, nhb, sl2, s.layout, nb);
   else {
     const int nqb2 = (s.Lq + 255) / 256;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb2 * nhb), dim3(512), 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
-                       s.Hk, s.Hq / s.Hk, nqb2, nhb, sl2);
+    const int64_t W = (int64_t)nqb2 * nhb;
+    if (CAUSAL ? W < kSplitCausalBelow : W <= kSplitFullUpTo)
+      hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(512), 0, stream,
+                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
+                         s.Hk, s.Hq / s.Hk, nqb, nhb, sl2);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb2 * nhb), dim3(512), 0, stream,
+                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
+                         s.Hk, s.Hq / s.Hk, nqb2, nhb, sl2);
   }
   return hipGetLastError();
 }

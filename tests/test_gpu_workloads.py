@@ -8,10 +8,11 @@ output):
   * permutations: bit-exact on whole destination-rank blocks and on head_to_seq;
   * forward: O and LSE of sampled rows -- hand-picked ones (both ends, tile
     edges, stressed rows) against the elementwise bar, uniformly drawn ones
-    also against the relative Frobenius bar -- and every row of a causal prefix: the kernel's rows below
-    L' do not depend on later tokens, so a run on the first L' tokens must
-    equal the first L' rows of the full run bit for bit, and is checked
-    in full against the oracle;
+    also against the relative Frobenius bar -- and every row of a causal
+    prefix: rows below L' do not depend on later tokens, so a run on the
+    first L' tokens equals the first L' rows of the full run bit for bit
+    (for an L' whose launch takes the full run's path), and a run on the
+    first 8192 tokens is checked in full against the oracle;
   * backward: dQ of the sampled rows (also prefix-checked), dK/dV of sampled
     key columns near the end, and over the full outputs the identities
     sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
@@ -223,46 +224,84 @@ def test_forward_sampled_rows(key):
             assert np.max(np.abs(lse[0, h, rows] - ref["lse"])) <= 1e-3
 
 
+# The dense forward splits each query block's key walk between two wave
+# groups when a causal launch has fewer than this many 256-row query blocks
+# (over all batch entries and heads); the split rounds differently, so a
+# prefix run is compared bit for bit with the full run only when both
+# launches take the same path.
+SPLIT_CAUSAL_BELOW = 384
+
+
+def _prefix_run(run, Lp):
+    """Attention (and backward) of rank 0's heads on the first Lp tokens."""
+    torch = torch_mod()
+    wl = run.wl
+    B, H, d, P, Hh, Hk = wl.B, wl.H, wl.d, wl.P, wl.Hp, wl.Hk
+    r0 = {n: run.head[n][0][:, :Lp] for n in run.ins}   # B = 1: the first Lp rows are contiguous
+    assert B == 1 and all(t.is_contiguous() for t in r0.values())
+    out = {"o": torch.empty((B, Lp, Hh, d), dtype=torch.bfloat16, device="cuda"),
+           "lse": torch.empty((B, Hh, Lp), dtype=torch.float32, device="cuda")}
+    lay_dev = None
+    if wl.block:   # the prefix's blocks keep their layout entries
+        nbp = Lp // wl.block
+        out["layout"] = np.ascontiguousarray(run.layout[:, :nbp, :nbp])
+        lay_dev = torch.from_numpy(out["layout"]).to("cuda")
+        U.ulysses_attn_fwd_block_sparse(r0["q"], r0["k"], r0["v"], out["o"], out["lse"], lay_dev, B, Lp, H, Hk, d,
+                                        P, True)
+    else:
+        U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], out["o"], out["lse"], B, Lp, Lp, H, Hk, d, P, True)
+    if wl.backward:
+        out["dq"] = torch.empty_like(out["o"])
+        out["dk"], out["dv"] = torch.empty_like(r0["k"]), torch.empty_like(r0["v"])
+        ws_bytes = (U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, Lp, H, Hk, d, P) if wl.block
+                    else U.ulysses_attn_bwd_gqa_workspace_bytes(B, Lp, Lp, H, Hk, d, P))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        if wl.block:
+            U.ulysses_attn_bwd_block_sparse(r0["q"], r0["k"], r0["v"], out["o"], r0["do"], out["lse"], out["dq"],
+                                            out["dk"], out["dv"], lay_dev, ws, B, Lp, H, Hk, d, P, True)
+        else:
+            U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], out["o"], r0["do"], out["lse"], out["dq"], out["dk"],
+                                   out["dv"], ws, B, Lp, Lp, H, Hk, d, P, True)
+    return out
+
+
+def _same_path_prefix(wl):
+    """Shortest prefix length >= PREFIX whose dense launch takes the full run's path."""
+    if wl.block:
+        return PREFIX
+    nhb = wl.B * wl.Hp
+    if -(-wl.L // 256) * nhb < SPLIT_CAUSAL_BELOW:
+        return PREFIX                                   # both launches split
+    return min(wl.L, max(PREFIX, -(-SPLIT_CAUSAL_BELOW // nhb) * 256))
+
+
 @pytest.mark.parametrize("key", [n for n in NAMES if WORKLOADS[n].causal])
 def test_causal_prefix_matches_full_run_and_oracle(key):
     torch = torch_mod()
     run = get_run(key)
     wl = run.wl
-    B, H, d, P, Hh, Hk = wl.B, wl.H, wl.d, wl.P, wl.Hp, wl.Hk
+    Hh = wl.Hp
+    # rows below Lb depend only on the first Lb tokens: a run on them equals
+    # the full run's rows bit for bit (O, LSE and, from the same O, dQ)
+    Lb = _same_path_prefix(wl)
+    same = _prefix_run(run, Lb)
+    full_o = run.ohead["o"][0][:, :Lb]
+    assert torch.equal(same["o"].view(torch.int16), full_o.view(torch.int16)), "prefix rows differ from the full run"
+    assert torch.equal(same["lse"], run.lse[:, :, :Lb].contiguous())
+    if wl.backward:
+        assert torch.equal(same["dq"].view(torch.int16), run.ohead["dq"][0][:, :Lb].view(torch.int16))
+    # the first PREFIX tokens as a problem of their own, in full against the oracle
     Lp = PREFIX
-    r0 = {n: run.head[n][0][:, :Lp] for n in run.ins}   # B = 1: the first Lp rows are contiguous
-    assert B == 1 and all(t.is_contiguous() for t in r0.values())
-    o = torch.empty((B, Lp, Hh, d), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((B, Hh, Lp), dtype=torch.float32, device="cuda")
-    if wl.block:   # the prefix's blocks keep their layout entries
-        nbp = Lp // wl.block
-        lay_p = np.ascontiguousarray(run.layout[:, :nbp, :nbp])
-        lay_dev = torch.from_numpy(lay_p).to("cuda")
-        U.ulysses_attn_fwd_block_sparse(r0["q"], r0["k"], r0["v"], o, lse, lay_dev, B, Lp, H, Hk, d, P, True)
-    else:
-        U.ulysses_attn_fwd_gqa(r0["q"], r0["k"], r0["v"], o, lse, B, Lp, Lp, H, Hk, d, P, True)
-    full_o = run.ohead["o"][0][:, :Lp]
-    assert torch.equal(o.view(torch.int16), full_o.view(torch.int16)), "prefix rows differ from the full run"
-    assert torch.equal(lse, run.lse[:, :, :Lp].contiguous())
+    pre = same if Lb == Lp else _prefix_run(run, Lp)
+    del same
+    o, lse = pre["o"], pre["lse"]
     q, k, v = (run.oracle_head(n)[:, :Lp] for n in "qkv")
     if wl.backward:
         do = run.oracle_head("do")[:, :Lp]
-        dq = torch.empty_like(o)
-        dk, dv = torch.empty_like(r0["k"]), torch.empty_like(r0["v"])
-        ws_bytes = (U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, Lp, H, Hk, d, P) if wl.block
-                    else U.ulysses_attn_bwd_gqa_workspace_bytes(B, Lp, Lp, H, Hk, d, P))
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        dq, dk, dv = pre["dq"], pre["dk"], pre["dv"]
         if wl.block:
-            U.ulysses_attn_bwd_block_sparse(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, lay_dev, ws, B,
-                                            Lp, H, Hk, d, P, True)
-        else:
-            U.ulysses_attn_bwd_gqa(r0["q"], r0["k"], r0["v"], o, r0["do"], lse, dq, dk, dv, ws, B, Lp, Lp, H, Hk, d,
-                                   P, True)
-        # dQ rows depend only on earlier keys: equal to the full run's
-        assert torch.equal(dq.view(torch.int16), run.ohead["dq"][0][:, :Lp].view(torch.int16))
-        if wl.block:
-            dq_r, dk_r, dv_r = oracle.attn_bwd_block_sparse(q, k, v, do, lay_p, wl.block, True)
-            o_r, lse_r = oracle.attn_fwd_block_sparse(q, k, v, lay_p, wl.block, True)
+            dq_r, dk_r, dv_r = oracle.attn_bwd_block_sparse(q, k, v, do, pre["layout"], wl.block, True)
+            o_r, lse_r = oracle.attn_fwd_block_sparse(q, k, v, pre["layout"], wl.block, True)
         else:
             dq_r, dk_r, dv_r = oracle.attn_bwd_gqa(q, k, v, do, True)
             o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
@@ -280,7 +319,7 @@ def test_causal_prefix_matches_full_run_and_oracle(key):
         check_close("dK prefix problem", to_f64(dk, "bf16"), dk_r, "bf16", allowed=allowed["dK"])
         check_close("dV prefix problem", to_f64(dv, "bf16"), dv_r, "bf16", allowed=allowed["dV"])
     elif wl.block:
-        o_r, lse_r = oracle.attn_fwd_block_sparse(q, k, v, lay_p, wl.block, True)
+        o_r, lse_r = oracle.attn_fwd_block_sparse(q, k, v, pre["layout"], wl.block, True)
     else:
         o_r, lse_r = oracle.attn_fwd_gqa(q, k, v, True)
     check_close("O prefix", to_f64(o, "bf16"), o_r, "bf16")
