@@ -21,6 +21,9 @@
 //   read transposed from LDS.
 // bf16 dQ kernel: workgroup = 4 waves x 32 query rows; the forward kernel's
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
+//   Launches of a few hundred query blocks use 8 waves per block instead,
+//   two groups that each walk half of its key tiles and add their dQ
+//   accumulators at the end (the longest block's walk sets their time).
 // Grouped-query attention (pinyu.ai, section "Head-count constraints"): a key
 //   head shared by G query heads gets the sum of their gradients; the dK/dV
 //   workgroup walks the query tiles of all G heads in turn and accumulates
@@ -507,20 +510,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
+// NG = 2 (dense launches too small to fill the chip): 8 waves, two groups
+// over the same 128 rows; group 0 walks the first half of the key tiles and
+// group 1 the second, each through its own K/V buffers, and group 0 adds
+// group 1's dQ accumulators to its own through LDS at the end.
+template <int D, bool CAUSAL, bool SPARSE, int NG = 1>
+__global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale,
     const uint8_t* __restrict__ layout, int nb) {
+  static_assert(NG == 1 || (NG == 2 && !SPARSE), "split key walks are for dense attention");
   constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256, RSTEP = 256 / CPR;
   constexpr int KST = Stride<D>::both;  // K: rows for S^T = K Q^T, transposed for dQ^T += K^T dS^T
   constexpr int VST = Stride<D>::row;   // V: rows for dP^T = V dO^T
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KST];
-  __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VST];
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2 * NG][BN * KST];
+  __shared__ __attribute__((aligned(16))) __bf16 Vs[2 * NG][BN * VST];
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;   // row group of this wave
+  const int grp = NG == 2 ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;   // key half (NG = 2)
   const int qb = nqb - 1 - (int)blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;         // (batch, query head) pair
   const int b = hb / Hq, h = hb - b * Hq;
@@ -556,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 
   const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int nkb = (kend + BN - 1) / BN;
-  const int srow = tid / CPR, scol = (tid % CPR) * 8;
+  const int srow = (tid & 255) / CPR, scol = (tid % CPR) * 8;
   const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vh, head_bytes);
@@ -576,8 +585,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      *reinterpret_cast<u32x4*>(&Ks[buf][(srow + j * RSTEP) * KST + scol]) = kreg[j];
-      *reinterpret_cast<u32x4*>(&Vs[buf][(srow + j * RSTEP) * VST + scol]) = vreg[j];
+      *reinterpret_cast<u32x4*>(&Ks[2 * grp + buf][(srow + j * RSTEP) * KST + scol]) = kreg[j];
+      *reinterpret_cast<u32x4*>(&Vs[2 * grp + buf][(srow + j * RSTEP) * VST + scol]) = vreg[j];
     }
   };
 
@@ -585,8 +594,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   // buffer (if store) and key tile next2 into the staging registers (if >= 0)
   auto tile = [&](int cur, int kb, bool store, int next2, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    const __bf16* Kc = Ks[cur];
-    const __bf16* Vc = Vs[cur];
+    const __bf16* Kc = Ks[2 * grp + cur];
+    const __bf16* Vc = Vs[2 * grp + cur];
     const int k0 = kb * BN;
     const bool edge = EDGE && (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk));
 #pragma unroll
@@ -644,7 +653,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const auto steady = std::integral_constant<bool, false>{};
   const auto edge = std::integral_constant<bool, true>{};
 
-  if constexpr (!SPARSE) {
+  if constexpr (!SPARSE && NG == 1) {
     load_tile(0);
     store_tile(0);
     __syncthreads();
@@ -654,6 +663,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     int kb = 0;
     for (; kb < nsteady; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, steady);
     for (; kb < nkb; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, edge);
+  } else if constexpr (!SPARSE) {
+    // this group's key tiles [t0, t0 + cnt); both groups pass `steps` barriers
+    const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
+    const int t0 = grp ? nkb / 2 : 0;
+    const int cnt = grp ? nkb - nkb / 2 : nkb / 2;
+    const int steps = nkb - nkb / 2;
+    if (cnt > 0) {
+      load_tile(t0);
+      store_tile(0);
+    }
+    __syncthreads();
+    if (cnt > 1) load_tile(t0 + 1);
+    int i = 0;
+    for (; i < cnt && t0 + i < nsteady; ++i)
+      tile(i & 1, t0 + i, i + 1 < cnt, i + 2 < cnt ? t0 + i + 2 : -1, steady);
+    for (; i < cnt; ++i) tile(i & 1, t0 + i, i + 1 < cnt, i + 2 < cnt ? t0 + i + 2 : -1, edge);
+    for (; i < steps; ++i) __syncthreads();   // group 0's idle step when nkb is odd
+    // every tile read ended at the last barrier: group 1's accumulators go
+    // through the K/V buffers to group 0
+    static_assert(4 * DT * 16 * 64 * 4 <= (int)(sizeof(Ks) + sizeof(Vs)), "merge exceeds the tile buffers");
+    float* rec = reinterpret_cast<float*>(&Ks[0][0]) + wave * (DT * 16 * 64);
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rec[(dt * 16 + e) * 64 + lane] = dqacc[dt][e];
+      }
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dqacc[dt][e] += rec[(dt * 16 + e) * 64 + lane];
+    }
   } else {
     // active key blocks of this query block, two key tiles each, as in the forward kernel
     LayoutScan scan;
@@ -854,6 +898,11 @@ size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char*
   return off;
 }
 
+// Dense dQ launches with few 128-row query blocks W split each block's key
+// walk between two wave groups (as the forward does for small launches).
+constexpr int64_t kDqSplitCausalBelow = 512;
+constexpr int64_t kDqSplitFullUpTo = 256;
+
 template <int D, bool CAUSAL>
 hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
                     void* dq, void* dk, void* dv, float* delta, const AttnShape& s, hipStream_t stream) {
@@ -893,6 +942,10 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, s.layout, nb);
+  else if ((int64_t)nqb * nhb < (CAUSAL ? kDqSplitCausalBelow : kDqSplitFullUpTo + 1))
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false, 2>), dim3((unsigned)nqb * nhb), dim3(512), 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0);
   else
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,

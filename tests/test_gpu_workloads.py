@@ -224,12 +224,13 @@ def test_forward_sampled_rows(key):
             assert np.max(np.abs(lse[0, h, rows] - ref["lse"])) <= 1e-3
 
 
-# The dense forward splits each query block's key walk between two wave
-# groups when a causal launch has fewer than this many 256-row query blocks
-# (over all batch entries and heads); the split rounds differently, so a
-# prefix run is compared bit for bit with the full run only when both
-# launches take the same path.
-SPLIT_CAUSAL_BELOW = 384
+# Dense causal launches split each query block's key walk between two wave
+# groups below these block counts (over all batch entries and heads): the
+# forward at 384 blocks of 256 rows, dQ at 512 blocks of 128 rows. The split
+# rounds differently, so a prefix run is compared bit for bit with the full
+# run only when its launches take the same paths.
+FWD_SPLIT_BELOW_256 = 384
+DQ_SPLIT_BELOW_128 = 512
 
 
 def _prefix_run(run, Lp):
@@ -266,13 +267,17 @@ def _prefix_run(run, Lp):
 
 
 def _same_path_prefix(wl):
-    """Shortest prefix length >= PREFIX whose dense launch takes the full run's path."""
+    """Shortest prefix length >= PREFIX whose dense launches take the full run's paths
+    (splitting is monotone: a launch below a threshold splits, and so does any shorter one)."""
     if wl.block:
         return PREFIX
     nhb = wl.B * wl.Hp
-    if -(-wl.L // 256) * nhb < SPLIT_CAUSAL_BELOW:
-        return PREFIX                                   # both launches split
-    return min(wl.L, max(PREFIX, -(-SPLIT_CAUSAL_BELOW // nhb) * 256))
+    Lb = PREFIX
+    if -(-wl.L // 256) * nhb >= FWD_SPLIT_BELOW_256:
+        Lb = max(Lb, -(-FWD_SPLIT_BELOW_256 // nhb) * 256)
+    if wl.backward and -(-wl.L // 128) * nhb >= DQ_SPLIT_BELOW_128:
+        Lb = max(Lb, -(-DQ_SPLIT_BELOW_128 // nhb) * 128)
+    return min(wl.L, -(-Lb // 256) * 256)
 
 
 @pytest.mark.parametrize("key", [n for n in NAMES if WORKLOADS[n].causal])
