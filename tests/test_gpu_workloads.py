@@ -399,26 +399,36 @@ def test_backward_identities_over_full_outputs(key):
         assert np.all(np.abs(sk) <= bound_k), (j, np.max(np.abs(sk) / bound_k))
 
 
-@pytest.mark.skipif(not os.environ.get("ULYSSES_FULL_ORACLE"),
-                    reason="every element against the fp64 oracle takes minutes of host time; "
-                           "set ULYSSES_FULL_ORACLE=1 to run it")
-@pytest.mark.parametrize("key", ["gpt7b-L131k"])
+_FULL_ONLY_ON_REQUEST = pytest.mark.skipif(
+    not os.environ.get("ULYSSES_FULL_ORACLE"),
+    reason="every element against the fp64 oracle takes minutes of host time; set ULYSSES_FULL_ORACLE=1 to run it")
+
+
+@pytest.mark.parametrize("key", ["gpt1.2b-L32k-fwd",
+                                 pytest.param("gpt7b-L131k", marks=_FULL_ONLY_ON_REQUEST)])
 def test_full_oracle_every_element(key):
-    """The 131K workload as the benchmark runs it, every element of O, LSE,
-    dQ, dK and dV of rank 0's heads against the full fp64 oracle (about a
-    minute of 16 host cores per head)."""
+    """A workload as the benchmark would run it, every element of rank 0's
+    O and LSE (and dQ, dK, dV) against the full fp64 oracle: seconds for the
+    32K forward, about a minute of 16 host cores per head for the 131K
+    forward and backward."""
     run = get_run(key)
     wl = run.wl
     assert run.G == 1
-    q, k, v, do = (run.oracle_head(n) for n in ("q", "k", "v", "do"))
-    got = {n: to_f64(run.ohead[n][0], "bf16") for n in ("o", "dq", "dk", "dv")}
+    q, k, v = (run.oracle_head(n) for n in ("q", "k", "v"))
+    do = run.oracle_head("do") if wl.backward else None
+    got = {n: to_f64(run.ohead[n][0], "bf16") for n in run.outs}
     lse = run.lse.cpu().numpy()
     for h in range(wl.Hp):
         t0 = time.perf_counter()
-        dq_r, dk_r, dv_r, o_r, lse_r, _ = oracle.attn_bwd_head(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h],
-                                                                wl.causal)
+        if wl.backward:
+            dq_r, dk_r, dv_r, o_r, lse_r, _ = oracle.attn_bwd_head(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h],
+                                                                    wl.causal)
+            want_all = (("o", o_r), ("dq", dq_r), ("dk", dk_r), ("dv", dv_r))
+        else:
+            o_r, lse_r = oracle.attn_fwd_head(q[0, :, h], k[0, :, h], v[0, :, h], wl.causal)
+            want_all = (("o", o_r),)
         print(f"[{key}] head {h}: oracle {time.perf_counter() - t0:.0f} s", flush=True)
-        for name, want in (("o", o_r), ("dq", dq_r), ("dk", dk_r), ("dv", dv_r)):
+        for name, want in want_all:
             st = check_close(f"{name} head {h}", got[name][0, :, h], want, "bf16")
             print(f"  {name}: max_abs {st['max_abs']:.3e} rel_fro {st['rel_fro']:.3e} "
                   f"max_err_over_allowed {st['max_err_over_allowed']:.3f}", flush=True)
