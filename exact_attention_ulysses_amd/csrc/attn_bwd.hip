@@ -23,7 +23,10 @@
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
 //   Launches of a few hundred query blocks use 8 waves per block instead,
 //   two groups that each walk half of its key tiles and add their dQ
-//   accumulators at the end (the longest block's walk sets their time).
+//   accumulators at the end (the longest block's walk sets their time);
+//   dK/dV launches of a few hundred key blocks likewise give each key
+//   block's walk to two workgroups, whose fp32 partial sums the block-layout
+//   reduce kernel adds.
 // Grouped-query attention (pinyu.ai, section "Head-count constraints"): a key
 //   head shared by G query heads gets the sum of their gradients; the dK/dV
 //   workgroup walks the query tiles of all G heads in turn and accumulates
@@ -173,17 +176,21 @@ __global__ __launch_bounds__(256) void bwd_sparse_plan_kernel(int ncol, int nlco
 // dK, dV of the split columns: the chunks' partial sums added in chunk order.
 // Work unit u: split column u / (D/4), and 1024/D of its 256 [dK | dV] rows
 // from row (1024/D) * (u mod (D/4)) on; each thread sums one 4-float group.
-template <int D>
+// DENSE: every one of the ndense dense work columns (kb * nb + hb, nb = head
+// pairs) has two chunks in slots 2c, 2c + 1.
+template <int D, bool DENSE = false>
 __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan, int nb, int Lk, int Hk,
                                                                 __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-                                                                float scale) {
+                                                                float scale, int ndense) {
   constexpr int UNITS = D / 4, ROWS = 1024 / D;   // units per split column, rows per unit
-  const int nunits = plan.header[1] * UNITS;
+  const int nunits = (DENSE ? ndense : plan.header[1]) * UNITS;
   const size_t rsk = (size_t)Hk * D;
   for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
     const int sp = u / UNITS;
-    const int col = plan.split_col[sp], slot = plan.split_slot[sp], nch = plan.split_nch[sp];
-    const int kb = col % nb, hb = col / nb;
+    const int col = DENSE ? sp : plan.split_col[sp];
+    const int slot = DENSE ? 2 * sp : plan.split_slot[sp];
+    const int nch = DENSE ? 2 : plan.split_nch[sp];
+    const int kb = DENSE ? col / nb : col % nb, hb = DENSE ? col % nb : col / nb;
     const int b = hb / Hk, hk = hb - b * Hk;
     const int row = (u - sp * UNITS) * ROWS + (int)threadIdx.x / (D / 4);   // of [dK | dV][128]
     const int c4 = ((int)threadIdx.x % (D / 4)) * 4;
@@ -215,7 +222,10 @@ __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan,
 // consumer's MFMAs do. Tiles are double buffered; each step ends with two
 // barriers (hand-over, then the staging of the next tile, which producers
 // (dO) and consumers (Q) share).
-template <int D, bool CAUSAL, bool SPARSE>
+// SPLIT (dense launches of few key blocks): workgroup 2c + h walks half h of
+// key-block column c's query tiles and leaves unscaled fp32 partial sums in
+// slot 2c + h, which the reduce kernel adds in order.
+template <int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -249,7 +259,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     nchunk = it.z;
     slot = it.w;
   }
-  if constexpr (!SPARSE) {
+  if constexpr (SPLIT) {
+    col = (int)blockIdx.x >> 1;
+    chunk = (int)blockIdx.x & 1;
+    nchunk = 2;
+    slot = 2 * col;
+  } else if constexpr (!SPARSE) {
     // jobs (key block kb, head pair hb) in order kb * nhb + hb, longest first.
     // Workgroup i runs on XCD i mod 8 (round-robin dispatch); each XCD takes
     // runs of 32 consecutive jobs, so that the workgroups sharing its L2 walk
@@ -277,6 +292,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   const int qstart = CAUSAL ? kb * 128 : 0;
   const int nqt = (Lq - qstart + BQ - 1) / BQ;   // query tiles per query head
   int nsteps = G * nqt;
+  int tbase = 0;   // first step of this workgroup's share of the walk (SPLIT)
+  if constexpr (SPLIT) {
+    tbase = chunk ? nsteps / 2 : 0;
+    nsteps = chunk ? nsteps - nsteps / 2 : nsteps / 2;
+  }
   // under the causal mask only the first two query tiles reach above a key of this block
   const int nmask = CAUSAL ? min(nqt, 2) : 0;
   if constexpr (SPARSE) {
@@ -324,8 +344,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       q0 = (2 * i + (t & 1)) * BQ;
       diag = CAUSAL && i == kb;
     } else {
-      g = (int)fdiv((uint32_t)t, fq);
-      const int qt = t - g * nqt;
+      g = (int)fdiv((uint32_t)(t + tbase), fq);
+      const int qt = t + tbase - g * nqt;
       q0 = qstart + qt * BQ;
       diag = CAUSAL && qt < nmask;
     }
@@ -476,7 +496,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       if (s + 2 < nsteps) load_tile(s + 2);
       __syncthreads();
     }
-    if (SPARSE && nchunk > 1) {
+    if ((SPARSE && nchunk > 1) || SPLIT) {
       // one chunk of a split column: unscaled fp32 partial sums, [dK | dV][128 keys][D],
       // summed in chunk order by the reduce kernel
       float* part = plan.partials + (size_t)(slot + chunk) * 2 * 128 * D;
@@ -872,18 +892,38 @@ hipError_t launch_delta(const T* o, const T* d_o, float* delta, const AttnShape&
 
 inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Dense bf16 dK/dV launches of few key-block columns C (over batch entries
+// and K/V heads) split every column's walk over the query tiles in two. One
+// workgroup per CU: under the causal mask the longest column is twice the
+// average, so a launch runs at about C / 512 of the chip without the split
+// and min(1, C / 256) with it (split below 512 columns); bidirectional
+// columns are equally long and pay once the halves still fit the CUs at once
+// (at most 128 columns).
+inline bool dkdv_split(const AttnShape& s) {
+  if (!s.bf16 || s.layout) return false;
+  const int64_t ncol = (int64_t)s.B * s.Hk * ((s.Lk + 127) / 128);
+  return s.causal ? ncol < 512 : ncol <= 128;
+}
+
 // Workspace: delta [B][Hq][Lq] fp32, then (block layouts only) the layout
 // columns' pair counts and lists, the plan and the partial-sum slots, each
 // 256-byte aligned.
 size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char* base) {
   const size_t ncol = (size_t)s.B * s.Hk * ((s.Lk + kSparseBlock - 1) / kSparseBlock);
   size_t off = round256((size_t)s.B * s.Hq * s.Lq * sizeof(float));
-  if (!sparse) return off;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
     off += round256(bytes);
     return p;
   };
+  if (!sparse) {
+    if (dkdv_split(s)) {
+      SparsePlan pl{};
+      pl.partials = (float*)take(2 * ncol * 2 * 128 * (size_t)s.D * sizeof(float));
+      if (plan) *plan = pl;
+    }
+    return off;
+  }
   const size_t nb = (s.Lk + kSparseBlock - 1) / kSparseBlock, nlcol = (size_t)s.Hk * nb;
   SparsePlan pl;
   pl.cnt = (int*)take(nlcol * sizeof(int));
@@ -926,7 +966,17 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
                        (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb, plan,
                        nkb);
     hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D>), dim3(1024), dim3(256), 0, stream, plan, nb, s.Lk, s.Hk,
-                       (__bf16*)dk, (__bf16*)dv, scale);
+                       (__bf16*)dk, (__bf16*)dv, scale, 0);
+  } else if (dkdv_split(s)) {
+    SparsePlan plan;
+    workspace_layout(s, false, &plan, reinterpret_cast<char*>(delta));
+    const int ncol = nkb * nkhb;
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false, true>), dim3((unsigned)(2 * ncol)), dim3(512), 0,
+                       stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0, plan,
+                       nkb);
+    hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D, true>), dim3(1024), dim3(256), 0, stream, plan, nkhb, s.Lk,
+                       s.Hk, (__bf16*)dk, (__bf16*)dv, scale, ncol);
   } else {
     const unsigned grid = (unsigned)((nkb * nkhb + 255) / 256 * 256);   // whole rounds of 256 jobs
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(512), 0, stream,

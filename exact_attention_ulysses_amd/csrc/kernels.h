@@ -30,6 +30,7 @@ struct AttnShape {
                 // key head h / (Hq / Hk)
   int D;        // head dim (64 or 128)
   bool causal;
+  bool bf16 = true;   // element type bf16 (else fp32)
   // block-sparse attention (bf16 only): per local query head uint8 layout
   // [Hq][nb][nb] over 128-token blocks, nb = ceil(L / 128); nullptr = dense
   const uint8_t* layout = nullptr;
@@ -42,7 +43,9 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
                                const AttnShape& s, hipStream_t stream);
 
 // workspace layout: delta [B][Hq][Lq] fp32; with a block layout also the
-// backward's work plan and partial-sum slots (all 256-byte aligned)
+// backward's work plan and partial-sum slots; for dense bf16 launches of few
+// key blocks the partial sums of their split key-block walks (all 256-byte
+// aligned)
 size_t attn_bwd_workspace_bytes(const AttnShape& s, bool sparse);
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const void* d_o, const float* lse, void* dq, void* dk, void* dv,

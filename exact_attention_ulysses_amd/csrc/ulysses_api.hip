@@ -141,6 +141,7 @@ int attn_dims(int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv, int64_
   s->Hk = (int)Hkl;
   s->D = (int)d_h;
   s->causal = causal == 1;
+  s->bf16 = dtype == ULYSSES_BF16;
   return ULYSSES_OK;
 }
 

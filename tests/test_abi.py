@@ -121,6 +121,29 @@ def test_workspace_size():
     assert lib.ulysses_attn_bwd_workspace_bytes(1, 100, 6, 64, 4, 1, U.BF16) == 0   # invalid sizes
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,L,H,d,P,causal,split", [
+    (1, 1024, 8, 128, 4, 1, True),        # 16 key-block columns
+    (1, 65408, 1, 128, 1, 1, True),       # 511 columns: causal split below 512
+    (1, 65536, 1, 128, 1, 1, False),      # 512 columns
+    (1, 16384, 1, 64, 1, 0, True),        # 128 columns: bidirectional split up to 128
+    (1, 16512, 1, 64, 1, 0, False),       # 129 columns
+])
+def test_dense_workspace_holds_split_partials(B, L, H, d, P, causal, split):
+    """bf16 launches of few key-block columns (batch x local K/V heads x
+    128-token key blocks) split each column's walk in two and need two
+    [dK | dV][128][d_h] fp32 partial sums per column after delta."""
+    lib = U.lib()
+    ncol = B * (H // P) * -(-L // 128)
+    want = _r256(B * (H // P) * L * 4) + (_r256(2 * ncol * 2 * 128 * d * 4) if split else 0)
+    assert lib.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, causal, U.BF16) == want
+    # fp32 never splits
+    assert lib.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, causal, U.FP32) == _r256(B * (H // P) * L * 4)
+
+
 def test_python_binding_rejects_mismatched_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(10)
