@@ -270,6 +270,44 @@ def attn_bwd_head(q, k, v, do, causal: bool, row_block: int = ROW_BLOCK):
     return dq, dk, dv, o, lse, D
 
 
+def attn_abs_sums_head(q, k, v, do, causal: bool, row_block: int = ROW_BLOCK):
+    """One head: the absolute-value sums behind each output of attn_bwd_head.
+
+    Every output element is a sum of products whose one factor a bf16
+    computation has to round (P in O = P V and dV = P^T dO, dS in dQ and
+    dK): for O_ie = sum_j P_ij v_je the sum is A_ie = sum_j P_ij |v_je|, and
+    likewise sum_i P_ij |dO_ie| for dV, sum_j |dS_ij| |k_je| / sqrt(d) for dQ
+    and sum_i |dS_ij| |q_ie| / sqrt(d) for dK. Rounding that factor to a
+    format with unit roundoff u changes the element by at most u * A (the
+    standard bound for a dot product with one perturbed factor). Returns
+    (a_dq, a_dk, a_dv, a_o), shaped like (dq, dk, dv, o). Test
+    infrastructure: it bounds rounding, it is not part of the method.
+    """
+    L, d = q.shape
+    Lkv = k.shape[0]
+    if causal and Lkv != L:
+        raise ValueError("causal attention needs Lq == Lkv")
+    scale = 1.0 / math.sqrt(d)
+    a_dq = np.zeros((L, d))
+    a_dk = np.zeros((Lkv, d))
+    a_dv = np.zeros((Lkv, d))
+    a_o = np.empty((L, d))
+    for i0 in range(0, L, row_block):
+        i1 = min(L, i0 + row_block)
+        nk = _visible_keys(i1, Lkv, causal)
+        s = _scores(q[i0:i1], k[:nk], i0, causal, scale)
+        p, _ = _softmax_rows(s)
+        a_o[i0:i1] = p @ np.abs(v[:nk])
+        dob = do[i0:i1]
+        ob = p @ v[:nk]
+        Db = np.sum(dob * ob, axis=1)
+        ads = np.abs(p * (dob @ v[:nk].T - Db[:, None]))
+        a_dq[i0:i1] = (ads @ np.abs(k[:nk])) * scale
+        a_dk[:nk] += (ads.T @ np.abs(q[i0:i1])) * scale
+        a_dv[:nk] += p.T @ np.abs(dob)
+    return a_dq, a_dk, a_dv, a_o
+
+
 def attn_bwd(q, k, v, do, causal: bool = True, row_block: int = ROW_BLOCK):
     """[B, L, Hh, d] float64 each -> (dq, dk, dv) [B, L, Hh, d], plus o, lse [B,Hh,L], D [B,Hh,L]."""
     B, L, Hh, d = q.shape

@@ -42,7 +42,7 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 8)
 
 
-def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, allowed=None):
+def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, allowed=None, abs_sum=None):
     """Compare a kernel output with the fp64 oracle value `want`.
 
     bf16 outputs: every element within max(1e-2, one bf16 ulp of the exact
@@ -52,7 +52,10 @@ def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, al
     elementwise bar applies (for hand-picked rows, whose norm says nothing
     about the whole tensor's relative Frobenius error). `allowed`, when given,
     replaces the elementwise bar with a per-element array (sums of several
-    outputs' budgets, see shared_head_allowed).
+    outputs' budgets, see shared_head_allowed). `abs_sum`, when given (bf16),
+    adds 2^-8 * abs_sum to the elementwise bar: the bound on rounding the
+    probabilities (or dS) to bf16 before they enter the products, from the
+    oracle's absolute sums (oracle.attn_abs_sums_head).
     """
     st = oracle.error_stats(got, want)
     if dtype == "bf16":
@@ -61,6 +64,8 @@ def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, al
         err = np.abs(np.asarray(got, dtype=np.float64) - want)
         if allowed is None:
             allowed = np.maximum(ma, bf16_ulp(want))
+        if abs_sum is not None:
+            allowed = allowed + 2.0 ** -8 * np.asarray(abs_sum, dtype=np.float64)
         st["max_err_over_allowed"] = float(np.max(err / allowed)) if err.size else 0.0
         ok = st["max_err_over_allowed"] <= 1.0 and (st["rel_fro"] <= rf or not fro)
     else:

@@ -379,6 +379,36 @@ def test_zero_query_closed_forms(Lq, Lk, causal):
         np.testing.assert_allclose(dv, r["dv"], rtol=1e-12, atol=1e-13)
 
 
+def _round_bf16(x):
+    return oracle.to_f64(f32_to_bf16_bits(np.asarray(x, np.float32)), "bf16")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_abs_sums_bound_operand_rounding(causal):
+    """attn_abs_sums_head bounds the effect of rounding P (for O, dV) and dS
+    (for dQ, dK) to bf16: recomputing each output with that factor rounded,
+    in fp64 otherwise, moves it by at most 2^-8 * A (bf16's unit roundoff
+    times the absolute sum), and A dominates the output itself."""
+    L, d = 70, 16
+    q, k, v, do = (_rand((L, d), s, 1.5) for s in (51, 52, 53, 54))
+    dq, dk, dv, o, lse, D = oracle.attn_bwd_head(q, k, v, do, causal, row_block=32)
+    a_dq, a_dk, a_dv, a_o = oracle.attn_abs_sums_head(q, k, v, do, causal, row_block=32)
+    scale = 1.0 / np.sqrt(d)
+    s = (q @ k.T) * scale
+    if causal:
+        s[np.triu_indices(L, 1)] = -np.inf
+    p = np.exp(s - lse[:, None])
+    ds = p * (do @ v.T - D[:, None])
+    pr, dsr = _round_bf16(p), _round_bf16(ds)
+    u = 2.0 ** -8
+    for name, exact, emul, a in (("O", o, pr @ v, a_o), ("dV", dv, pr.T @ do, a_dv),
+                                 ("dQ", dq, (dsr @ k) * scale, a_dq), ("dK", dk, (dsr.T @ q) * scale, a_dk)):
+        assert np.all(np.abs(emul - exact) <= u * a + 1e-12), name
+        assert np.all(np.abs(exact) <= a + 1e-12), name
+        # the bound is not vacuous: rounding moves some element by a tenth of it or more
+        assert np.max(np.abs(emul - exact) / (u * a + 1e-300)) > 0.1, name
+
+
 # ---------------------------------------------------------------------------
 # sampled evaluation agrees with the full oracle
 # ---------------------------------------------------------------------------
