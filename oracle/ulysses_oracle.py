@@ -479,6 +479,28 @@ def attn_bwd_block_sparse_head(q, k, v, do, layout, block: int, causal: bool):
     return dq, dk, dv, o, lse, D
 
 
+def attn_abs_sums_block_sparse_head(q, k, v, do, layout, block: int, causal: bool):
+    """attn_abs_sums_head under a block layout: the absolute-value sums of the
+    products behind each output of attn_bwd_block_sparse_head (P for O and
+    dV, dS for dQ and dK, over the visible pairs). Test infrastructure."""
+    L, d = q.shape
+    scale = 1.0 / math.sqrt(d)
+    a_dq, a_dk, a_dv, a_o = np.zeros((L, d)), np.zeros((L, d)), np.zeros((L, d)), np.zeros((L, d))
+    for bi, i0 in enumerate(range(0, L, block)):
+        i1 = min(L, i0 + block)
+        vis = block_visible(layout[bi], block, i0, i1, L, causal)
+        s = (q[i0:i1] @ k.T) * scale
+        p, _ = _masked_softmax_rows(s, vis)
+        a_o[i0:i1] = p @ np.abs(v)
+        ob = p @ v
+        Db = np.sum(do[i0:i1] * ob, axis=1)
+        ads = np.abs(p * (do[i0:i1] @ v.T - Db[:, None]))
+        a_dv += p.T @ np.abs(do[i0:i1])
+        a_dq[i0:i1] = (ads @ np.abs(k)) * scale
+        a_dk += (ads.T @ np.abs(q[i0:i1])) * scale
+    return a_dq, a_dk, a_dv, a_o
+
+
 def attn_fwd_block_sparse(q, k, v, layout, block: int, causal: bool = True):
     """q, k, v [B, L, H, d] (one rank's heads); layout [H, nb, nb] shared by the
     batch. Returns O [B, L, H, d] and LSE [B, H, L]."""

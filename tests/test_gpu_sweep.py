@@ -6,7 +6,9 @@ dim 64 or 128, causal or bidirectional (cross-attention when the lengths
 differ), bf16 or fp32. Most of them are small launches, which the kernels
 run with split key and query walks; the wide cases (many heads over few
 tokens) reach the single-walk schedules at sizes the oracle still finishes
-in a moment. Forward and backward go through the generalised entry points
+in a moment. Twelve more cases run block layouts (a window, global and
+random blocks per row, some block rows emptied; bf16, self-attention).
+Forward and backward go through the generalised entry points
 and are held to the same bars as every other parity test, with the bf16
 elementwise bar widened by the bound on rounding P and dS to bf16 inside the
 products (2^-8 times the oracle's absolute sums): without it the dV of the
@@ -19,7 +21,7 @@ import pytest
 
 import exact_attention_ulysses_amd as U
 import oracle
-from workloads import custom, host_tensor
+from workloads import block_layout, custom, host_tensor
 
 from gpu_common import LSE_ABS, check_close, shared_head_allowed, to_device, to_f64, torch_mod
 
@@ -118,4 +120,77 @@ def test_sweep_parity(case):
     for name, got, want in (("dK", dk, dk_r), ("dV", dv, dv_r)):
         allowed = shared_head_allowed(parts[name], want, dtype) if dtype == "bf16" else None
         check_close(f"{name} {tag}", to_f64(got, dtype), want, dtype, allowed=allowed,
+                    abs_sum=asum[name.lower()])
+
+
+def _draw_sparse_case(i):
+    rng = np.random.default_rng(9000 + i)
+    causal = bool(rng.integers(0, 2))
+    P = int(rng.integers(1, 3))
+    Hkl = int(rng.choice([1, 2]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(1, 3))
+    L = int(rng.integers(1, 1500))
+    d = int(rng.choice([64, 128]))
+    lay = (int(rng.integers(1, 5)), int(rng.integers(0, 3)), int(rng.integers(0, 4)), bool(rng.integers(0, 2)))
+    return B, L, Hkl * G * P, Hkl * P, d, P, causal, lay   # lay: window, global, random, empty rows
+
+
+SPARSE_CASES = [_draw_sparse_case(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
+def test_sweep_block_sparse_parity(case):
+    """Block layouts over random sizes: a window, global and random blocks per
+    row (and, in some cases, block rows emptied), bf16."""
+    B, L, Hq, Hkv, d, P, causal, (window, n_global, n_random, empty) = SPARSE_CASES[case]
+    torch = torch_mod()
+    Hql, Hkl = Hq // P, U.kv_local_heads(Hkv, P)
+    G = Hql // Hkl
+    BLOCK = U.SPARSE_BLOCK
+    base = 8000 + case
+    host = {n: _draw(B, L, Hql, d, "bf16", n, base) for n in ("q", "do")}
+    host.update({n: _draw(B, L, Hkl, d, "bf16", n, base) for n in ("k", "v")})
+    lay = block_layout(custom(B, L, Hql, d, 1, causal=causal, index=base, block=BLOCK, window=window,
+                              n_global=n_global, n_random=n_random))
+    nb = lay.shape[1]
+    if empty:   # rows that see nothing: zero output, LSE -inf, no gradient through them
+        lay[:, nb // 2, :] = 0
+    dev = {n: to_device(host[n], "bf16") for n in host}
+    layout = torch.from_numpy(lay).to("cuda")
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((B, Hql, L), dtype=torch.float32, device="cuda")
+    U.ulysses_attn_fwd_block_sparse(dev["q"], dev["k"], dev["v"], o, lse, layout, B, L, Hq, Hkv, d, P, causal)
+    dq = torch.empty_like(dev["q"])
+    dk, dv = torch.empty_like(dev["k"]), torch.empty_like(dev["v"])
+    ws = torch.empty(U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, Hq, Hkv, d, P, causal),
+                     dtype=torch.uint8, device="cuda")
+    U.ulysses_attn_bwd_block_sparse(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, dq, dk, dv, layout, ws, B, L,
+                                    Hq, Hkv, d, P, causal)
+    torch.cuda.synchronize()
+    tag = f"sparse case {case} {SPARSE_CASES[case]}"
+    f = {n: oracle.to_f64(host[n], "bf16") for n in host}
+    kr, vr = np.repeat(f["k"], G, axis=2), np.repeat(f["v"], G, axis=2)
+    o_r, lse_r = oracle.attn_fwd_block_sparse(f["q"], kr, vr, lay, BLOCK, causal)
+    dq_r, dk_rep, dv_rep = oracle.attn_bwd_block_sparse(f["q"], kr, vr, f["do"], lay, BLOCK, causal)
+    asum = {"o": np.zeros(f["q"].shape), "dq": np.zeros(f["q"].shape),
+            "dk": np.zeros(f["k"].shape), "dv": np.zeros(f["v"].shape)}
+    for b in range(B):
+        for h in range(Hql):
+            a_dq, a_dk, a_dv, a_o = oracle.attn_abs_sums_block_sparse_head(
+                f["q"][b, :, h], f["k"][b, :, h // G], f["v"][b, :, h // G], f["do"][b, :, h], lay[h], BLOCK, causal)
+            asum["o"][b, :, h], asum["dq"][b, :, h] = a_o, a_dq
+            asum["dk"][b, :, h // G] += a_dk
+            asum["dv"][b, :, h // G] += a_dv
+    check_close(f"O {tag}", to_f64(o, "bf16"), o_r, "bf16", abs_sum=asum["o"])
+    lse_g = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lse_g), np.isneginf(lse_r)), f"LSE -inf rows {tag}"
+    fin = np.isfinite(lse_r)
+    assert np.max(np.abs(lse_g[fin] - lse_r[fin]), initial=0.0) <= LSE_ABS["bf16"], f"LSE {tag}"
+    check_close(f"dQ {tag}", to_f64(dq, "bf16"), dq_r, "bf16", abs_sum=asum["dq"])
+    for name, rep in (("dK", dk_rep), ("dV", dv_rep)):
+        parts = np.moveaxis(rep.reshape(B, L, Hkl, G, d), 3, 0)   # [G, B, L, Hkl, d]
+        want = parts.sum(axis=0)
+        allowed = None if G == 1 else shared_head_allowed(parts, want, "bf16")
+        check_close(f"{name} {tag}", to_f64(dk if name == "dK" else dv, "bf16"), want, "bf16", allowed=allowed,
                     abs_sum=asum[name.lower()])

@@ -409,6 +409,40 @@ def test_abs_sums_bound_operand_rounding(causal):
         assert np.max(np.abs(emul - exact) / (u * a + 1e-300)) > 0.1, name
 
 
+def test_block_sparse_abs_sums_bound_operand_rounding():
+    """The block-layout absolute sums bound the same rounding under a sparse
+    layout (visibility from the layout expanded to tokens, causal inside)."""
+    L, d, block = 300, 16, 128
+    q, k, v, do = (_rand((L, d), s, 1.5) for s in (71, 72, 73, 74))
+    lay = np.array([[1, 0, 0], [0, 1, 0], [1, 1, 1]], np.uint8)
+    dq, dk, dv, o, lse, D = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, True)
+    a_dq, a_dk, a_dv, a_o = oracle.attn_abs_sums_block_sparse_head(q, k, v, do, lay, block, True)
+    vis = np.kron(lay, np.ones((block, block), np.uint8))[:L, :L].astype(bool) & np.tri(L, dtype=bool)
+    s = np.where(vis, (q @ k.T) / np.sqrt(d), -np.inf)
+    p = np.exp(s - lse[:, None])
+    ds = p * (do @ v.T - D[:, None])
+    pr, dsr = _round_bf16(p), _round_bf16(ds)
+    u = 2.0 ** -8
+    for name, exact, emul, a in (("O", o, pr @ v, a_o), ("dV", dv, pr.T @ do, a_dv),
+                                 ("dQ", dq, (dsr @ k) / np.sqrt(d), a_dq), ("dK", dk, (dsr.T @ q) / np.sqrt(d), a_dk)):
+        assert np.all(np.abs(emul - exact) <= u * a + 1e-12), name
+        assert np.all(np.abs(exact) <= a + 1e-12), name
+
+
+def test_abs_sums_under_a_full_layout_equal_the_dense_ones():
+    """With every block of the layout set, the block-sparse absolute sums are
+    the dense ones (the layout only removes pairs)."""
+    L, d, block = 300, 16, 128
+    q, k, v, do = (_rand((L, d), s) for s in (61, 62, 63, 64))
+    nb = -(-L // block)
+    full = np.ones((nb, nb), np.uint8)
+    for causal in (True, False):
+        dense = oracle.attn_abs_sums_head(q, k, v, do, causal)
+        sparse = oracle.attn_abs_sums_block_sparse_head(q, k, v, do, full, block, causal)
+        for a, b in zip(dense, sparse):
+            np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # sampled evaluation agrees with the full oracle
 # ---------------------------------------------------------------------------
