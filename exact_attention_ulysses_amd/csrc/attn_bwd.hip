@@ -23,7 +23,10 @@
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
 //   Launches of a few hundred query blocks use 8 waves per block instead,
 //   two groups that each walk half of its key tiles and add their dQ
-//   accumulators at the end (the longest block's walk sets their time);
+//   accumulators at the end (the longest block's walk sets their time), or
+//   cut every block's walk into chunks run by separate workgroups whose fp32
+//   partial sums a reduce kernel adds in chunk order, whichever a cost model
+//   of the launch ranks faster;
 //   dK/dV launches of a few hundred key blocks likewise give each key
 //   block's walk to two workgroups, whose fp32 partial sums the block-layout
 //   reduce kernel adds.
@@ -37,6 +40,8 @@
 //   whose fp32 partial sums a last kernel adds in a fixed order.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "block_sparse.h"
@@ -49,6 +54,14 @@ namespace ulysses {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// S(m) = sum over x = 1..m of ceil(x / t): the number of chunks of query
+// blocks 0..m-1 when block x - 1 (2x key tiles of 64 under the causal mask)
+// is cut into ceil(x / t) parts of at most 2t tiles.
+__host__ __device__ inline int chunk_prefix(int m, int t) {
+  const int a = m / t, r = m - a * t;
+  return t * a * (a + 1) / 2 + r * (a + 1);
+}
 
 // delta[b][h][i] = sum_e dO[b][i][h][e] * O[b][i][h][e]; D/8 lanes per row.
 template <typename T, int D>
@@ -534,13 +547,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
 // over the same 128 rows; group 0 walks the first half of the key tiles and
 // group 1 the second, each through its own K/V buffers, and group 0 adds
 // group 1's dQ accumulators to its own through LDS at the end.
-template <int D, bool CAUSAL, bool SPARSE, int NG = 1>
+template <int D, bool CAUSAL, bool SPARSE, int NG = 1, bool CHUNK = false>
 __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale,
-    const uint8_t* __restrict__ layout, int nb) {
+    const uint8_t* __restrict__ layout, int nb, int ck, float* __restrict__ part) {
   static_assert(NG == 1 || (NG == 2 && !SPARSE), "split key walks are for dense attention");
+  static_assert(!CHUNK || (NG == 1 && !SPARSE), "chunked key walks are for dense attention");
   constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256, RSTEP = 256 / CPR;
   constexpr int KST = Stride<D>::both;  // K: rows for S^T = K Q^T, transposed for dQ^T += K^T dS^T
   constexpr int VST = Stride<D>::row;   // V: rows for dP^T = V dO^T
@@ -550,8 +564,38 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;   // row group of this wave
   const int grp = NG == 2 ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;   // key half (NG = 2)
-  const int qb = nqb - 1 - (int)blockIdx.x / nhb;
-  const int hb = blockIdx.x % nhb;         // (batch, query head) pair
+  int qb = nqb - 1 - (int)blockIdx.x / nhb;
+  int hb = blockIdx.x % nhb;               // (batch, query head) pair
+  int chunk = 0, nchunk = 1;               // this workgroup's part of the block's key walk (CHUNK)
+  if constexpr (CHUNK) {
+    const int i = blockIdx.x;
+    if constexpr (CAUSAL) {
+      // block qb = x - 1 has ceil(x / ck) chunks; blocks run longest first,
+      // so the work items before block x number nhb (S(nqb) - S(x)) with
+      // S(m) = chunk_prefix(m, ck); the block holding item i is the smallest
+      // x whose predecessors number at most i
+      const int sn = chunk_prefix(nqb, ck);
+      int lo = 1, hi = nqb;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (nhb * (sn - chunk_prefix(mid, ck)) <= i)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      nchunk = (lo + ck - 1) / ck;
+      const int loc = i - nhb * (sn - chunk_prefix(lo, ck));
+      qb = lo - 1;
+      hb = loc / nchunk;
+      chunk = loc - hb * nchunk;
+    } else {
+      nchunk = ck;   // every block: ck chunks
+      const int bi = i / nchunk;
+      chunk = i - bi * nchunk;
+      qb = nqb - 1 - bi / nhb;
+      hb = bi % nhb;
+    }
+  }
   const int b = hb / Hq, h = hb - b * Hq;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
   const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
@@ -673,7 +717,19 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
   const auto steady = std::integral_constant<bool, false>{};
   const auto edge = std::integral_constant<bool, true>{};
 
-  if constexpr (!SPARSE && NG == 1) {
+  if constexpr (CHUNK) {
+    // key tiles [t0, t1): part `chunk` of `nchunk` near-equal parts of the walk
+    const int t0 = chunk * nkb / nchunk, cnt = (chunk + 1) * nkb / nchunk - t0;
+    const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
+    load_tile(t0);
+    store_tile(0);
+    __syncthreads();
+    if (cnt > 1) load_tile(t0 + 1);
+    int i = 0;
+    for (; i < cnt && t0 + i < nsteady; ++i)
+      tile(i & 1, t0 + i, i + 1 < cnt, i + 2 < cnt ? t0 + i + 2 : -1, steady);
+    for (; i < cnt; ++i) tile(i & 1, t0 + i, i + 1 < cnt, i + 2 < cnt ? t0 + i + 2 : -1, edge);
+  } else if constexpr (!SPARSE && NG == 1) {
     load_tile(0);
     store_tile(0);
     __syncthreads();
@@ -741,13 +797,58 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
     }
   }
 
-  if (valid) {
+  if constexpr (CHUNK) {
+    // unscaled fp32 partial sums of the block's 128 rows in slot blockIdx.x,
+    // [128][D]; the reduce kernel adds a block's slots in chunk order
+    float* prow = part + ((size_t)blockIdx.x * 128 + 32 * wave + l32) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = dqacc[dt][4 * a + i];
+        *reinterpret_cast<f32x4*>(prow + 32 * dt + 8 * a + 4 * hl) = v4;
+      }
+    }
+  } else if (valid) {
     __bf16* row = dq + qoff + (size_t)qrow * rsq;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<bf16x4*>(row + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dqacc[dt], a, scale);
+    }
+  }
+}
+
+// Chunked dQ: block (x = query block + 1, head pair hb) owns ceil(x / ck)
+// consecutive slots (causal; ck per block when bidirectional), in the order
+// the dQ kernel numbers its work items; their sum, scaled and rounded once,
+// is the block's dQ.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ part, __bf16* __restrict__ dq,
+                                                            int Lq, int Hq, int nqb, int nhb, int ck, float scale) {
+  constexpr int UNITS = 128 * D / 1024, ROWS = 1024 / D;   // units per block, rows per unit
+  const int nunits = nqb * nhb * UNITS;
+  const int sn = CAUSAL ? chunk_prefix(nqb, ck) : 0;
+  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const int bi = u / UNITS;                    // blocks longest first, head pairs inner
+    const int x = nqb - bi / nhb, hb = bi % nhb;
+    const int nch = CAUSAL ? (x + ck - 1) / ck : ck;
+    const int base = CAUSAL ? nhb * (sn - chunk_prefix(x, ck)) + hb * nch : bi * nch;
+    const int row = (u - bi * UNITS) * ROWS + (int)threadIdx.x / (D / 4);
+    const int c4 = ((int)threadIdx.x % (D / 4)) * 4;
+    f32x4 acc = f32x4{};
+    for (int j = 0; j < nch; ++j)
+      acc += *reinterpret_cast<const f32x4*>(part + ((size_t)(base + j) * 128 + row) * D + c4);
+    const int qrow = (x - 1) * 128 + row;
+    if (qrow < Lq) {
+      const int b = hb / Hq, h = hb - b * Hq;
+      bf16x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = (__bf16)(acc[i] * scale);
+      *reinterpret_cast<bf16x4*>(dq + (((size_t)b * Lq + qrow) * Hq + h) * D + c4) = o;
     }
   }
 }
@@ -905,10 +1006,71 @@ inline bool dkdv_split(const AttnShape& s) {
   return s.causal ? ncol < 512 : ncol <= 128;
 }
 
-// Workspace: delta [B][Hq][Lq] fp32, then (block layouts only) the layout
-// columns' pair counts and lists, the plan and the partial-sum slots, each
-// 256-byte aligned.
-size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char* base) {
+// Dense dQ launches with few 128-row query blocks W split each block's key
+// walk between two wave groups of one workgroup (as the forward does for
+// small launches), or cut it into chunks (below).
+constexpr int64_t kDqSplitCausalBelow = 512;
+constexpr int64_t kDqSplitFullUpTo = 256;
+
+// Dense bf16 dQ launches of few 128-row query blocks can instead cut every
+// block's walk over its key tiles into chunks that separate workgroups run
+// (two per CU, 512 at once), each leaving unscaled fp32 partial sums in a
+// slot of the workspace that a reduce kernel adds in chunk order. Under the
+// causal mask block qb has 2(qb + 1) tiles of 64 keys: whole walks leave the
+// longest block setting the time of a launch of up to ~1000 blocks (twice
+// the balanced time or more), while ceil((qb + 1) / t) near-equal parts of
+// block qb make every work item at most 2t tiles long. The host takes the
+// t (bidirectional: parts per block) that a cost model in tile steps ranks
+// best -- critical path (the longest item when all fit in one round of 512
+// workgroups, else the average load of a slot plus half an item), start-up
+// per round, partial-sum traffic and the extra launch -- and cuts only where
+// that beats the whole walks by 10 %.
+struct DqChunks {
+  int ck = 0;      // t (causal) or parts per block (bidirectional); 0: whole walks
+  int items = 0;   // work items, one partial-sum slot each
+};
+constexpr int kDqSlots = 512;
+constexpr int kDqMaxItems = 4 * kDqSlots;
+
+inline DqChunks dq_chunks(const AttnShape& s) {
+  DqChunks best;
+  if (!s.bf16 || s.layout) return best;
+  const int64_t nqb = (s.Lq + 127) / 128, nhb = (int64_t)s.B * s.Hq, W = nqb * nhb;
+  const int64_t nkt = (s.Lk + 63) / 64;   // key tiles of the longest block
+  if (W >= kDqMaxItems) return best;
+  const double total = s.causal ? (double)nhb * (nqb * (nqb - 1) + nkt) : (double)W * nkt;
+  const double avg = total / kDqSlots;
+  auto rounds = [](int64_t n, int64_t per) { return (double)((n + per - 1) / per); };
+  // whole walks: two wave groups per block below the thresholds above, else one
+  const bool ng2 = s.causal ? W < kDqSplitCausalBelow : W <= kDqSplitFullUpTo;
+  const double whole = ng2 ? std::max((double)((nkt + 1) / 2), avg) + 2 * rounds(W, 256)
+                           : std::max((double)nkt, avg) + 2 * rounds(W, kDqSlots);
+  double best_cost = 0.9 * whole;
+  auto consider = [&](int64_t ck, int64_t items, int64_t longest) {
+    if (items > kDqMaxItems) return;
+    // one round: every item has a slot of its own
+    const double path = items <= kDqSlots ? (double)longest : std::max((double)longest, avg + 0.5 * longest);
+    const double cost = path + 2 * rounds(items, kDqSlots) + items / 64.0 + 3;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best.ck = (int)ck;
+      best.items = (int)items;
+    }
+  };
+  if (s.causal) {
+    for (int64_t t = 1; t < nqb; ++t)
+      consider(t, nhb * chunk_prefix((int)nqb, (int)t), std::min(2 * t, nkt));
+  } else {
+    for (int64_t c = 2; c <= nkt && W * c <= kDqMaxItems; ++c) consider(c, W * c, (nkt + c - 1) / c);
+  }
+  return best;
+}
+
+// Workspace: delta [B][Hq][Lq] fp32, then (dense) the dK/dV and the dQ
+// partial-sum slots of launches that split their walks, or (block layouts)
+// the layout columns' pair counts and lists, the plan and the partial-sum
+// slots, each 256-byte aligned.
+size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char* base, float** dq_part = nullptr) {
   const size_t ncol = (size_t)s.B * s.Hk * ((s.Lk + kSparseBlock - 1) / kSparseBlock);
   size_t off = round256((size_t)s.B * s.Hq * s.Lq * sizeof(float));
   auto take = [&](size_t bytes) {
@@ -921,6 +1083,11 @@ size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char*
       SparsePlan pl{};
       pl.partials = (float*)take(2 * ncol * 2 * 128 * (size_t)s.D * sizeof(float));
       if (plan) *plan = pl;
+    }
+    const DqChunks dc = dq_chunks(s);
+    if (dc.items) {
+      float* p = (float*)take((size_t)dc.items * 128 * s.D * sizeof(float));
+      if (dq_part) *dq_part = p;
     }
     return off;
   }
@@ -937,11 +1104,6 @@ size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char*
   if (plan) *plan = pl;
   return off;
 }
-
-// Dense dQ launches with few 128-row query blocks W split each block's key
-// walk between two wave groups (as the forward does for small launches).
-constexpr int64_t kDqSplitCausalBelow = 512;
-constexpr int64_t kDqSplitFullUpTo = 256;
 
 template <int D, bool CAUSAL>
 hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
@@ -988,18 +1150,30 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
   if (e != hipSuccess) return e;
   const int nhb = s.B * s.Hq;
   const int nqb = (s.Lq + 127) / 128;
+  const DqChunks dc = dq_chunks(s);
   if (s.layout)
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, s.layout, nb);
-  else if ((int64_t)nqb * nhb < (CAUSAL ? kDqSplitCausalBelow : kDqSplitFullUpTo + 1))
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, s.layout, nb, 0, nullptr);
+  else if (dc.items) {
+    float* part = nullptr;
+    workspace_layout(s, false, nullptr, reinterpret_cast<char*>(delta), &part);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false, 1, true>), dim3((unsigned)dc.items), dim3(256), 0,
+                       stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, dc.ck, part);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned units = (unsigned)nqb * nhb * (128 * D / 1024);
+    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D, CAUSAL>), dim3(std::min(units, 2048u)), dim3(256), 0, stream, part,
+                       (__bf16*)dq, s.Lq, s.Hq, nqb, nhb, dc.ck, scale);
+  } else if ((int64_t)nqb * nhb < (CAUSAL ? kDqSplitCausalBelow : kDqSplitFullUpTo + 1))
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false, 2>), dim3((unsigned)nqb * nhb), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0);
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, 0, nullptr);
   else
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0);
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, 0, nullptr);
   return hipGetLastError();
 }
 

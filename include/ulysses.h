@@ -169,10 +169,13 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * Workspace ulysses_attn_bwd needs for these sizes (0 if the sizes are
- * invalid): delta [B][H/P][L] fp32, and for bf16 launches of few key-block
+ * invalid): delta [B][H/P][L] fp32; for bf16 launches of few key-block
  * columns (B x local heads x ceil(L / 128): causal below 512, bidirectional
  * up to 128) two fp32 partial sums [dK | dV][128][d_h] per column, so that
- * two workgroups can share each column's walk.
+ * two workgroups can share each column's walk; and for bf16 launches of few
+ * 128-row query blocks (fewer than 2048 over B x local heads, where cutting
+ * the blocks' key walks into chunks pays) one fp32 [128][d_h] partial sum per
+ * chunk, at most 2048 chunks (128 MiB at d_h = 128).
  */
 size_t ulysses_attn_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t d_h,
                                         int64_t P, int causal, int dtype);

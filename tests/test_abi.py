@@ -11,6 +11,7 @@ import re
 import pytest
 
 import exact_attention_ulysses_amd as U
+from plans import dq_chunk_items as _dq_chunk_items
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ulysses.h")
 
@@ -125,6 +126,31 @@ def _r256(x):
     return (x + 255) // 256 * 256
 
 
+@pytest.mark.parametrize("B,L,H,causal,chunked", [
+    (1, 4096, 4, True, True), (1, 8192, 4, True, True), (1, 16384, 2, True, True),
+    (1, 65536, 1, True, True),            # 512 blocks: four rounds of chunks
+    (1, 32768, 4, True, False),           # 1024 blocks: whole walks
+    (1, 131072, 4, True, False),
+    (1, 4096, 8, True, False),            # 256 blocks: two wave groups per block rank better
+    (1, 16384, 1, False, True), (2, 4096, 2, False, True), (2, 1000, 3, False, False),
+    (2, 3000, 3, True, True), (1, 1, 1, True, False),
+])
+def test_dense_workspace_holds_dq_chunks(B, L, H, causal, chunked):
+    """bf16 dQ launches of few query blocks cut the blocks' key walks into
+    chunks, one [128][d_h] fp32 partial-sum slot each, after delta and any
+    dK/dV partial sums; the item count the library sizes its workspace for
+    is the one planned above."""
+    lib = U.lib()
+    for d in (64, 128):
+        items = _dq_chunk_items(B, L, L, H, causal)
+        assert (items > 0) == chunked
+        base = lib.ulysses_attn_bwd_workspace_bytes(B, L, H, d, 1, causal, U.FP32)   # delta only
+        ncol = B * H * -(-L // 128)
+        kv = _r256(2 * ncol * 2 * 128 * d * 4) if (ncol < 512 if causal else ncol <= 128) else 0
+        want = base + kv + _r256(items * 128 * d * 4)
+        assert lib.ulysses_attn_bwd_workspace_bytes(B, L, H, d, 1, causal, U.BF16) == want, (d, items)
+
+
 @pytest.mark.parametrize("B,L,H,d,P,causal,split", [
     (1, 1024, 8, 128, 4, 1, True),        # 16 key-block columns
     (1, 65408, 1, 128, 1, 1, True),       # 511 columns: causal split below 512
@@ -135,10 +161,12 @@ def _r256(x):
 def test_dense_workspace_holds_split_partials(B, L, H, d, P, causal, split):
     """bf16 launches of few key-block columns (batch x local K/V heads x
     128-token key blocks) split each column's walk in two and need two
-    [dK | dV][128][d_h] fp32 partial sums per column after delta."""
+    [dK | dV][128][d_h] fp32 partial sums per column after delta (and the dQ
+    chunks' partial sums after those)."""
     lib = U.lib()
     ncol = B * (H // P) * -(-L // 128)
     want = _r256(B * (H // P) * L * 4) + (_r256(2 * ncol * 2 * 128 * d * 4) if split else 0)
+    want += _r256(_dq_chunk_items(B, L, L, H // P, causal) * 128 * d * 4)
     assert lib.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, causal, U.BF16) == want
     # fp32 never splits
     assert lib.ulysses_attn_bwd_workspace_bytes(B, L, H, d, P, causal, U.FP32) == _r256(B * (H // P) * L * 4)

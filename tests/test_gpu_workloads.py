@@ -226,13 +226,14 @@ def test_forward_sampled_rows(key):
             assert np.max(np.abs(lse[0, h, rows] - ref["lse"])) <= 1e-3
 
 
-# Dense causal launches split each query block's key walk between two wave
-# groups below these block counts (over all batch entries and heads): the
-# forward at 384 blocks of 256 rows, dQ at 512 blocks of 128 rows. The split
-# rounds differently, so a prefix run is compared bit for bit with the full
-# run only when its launches take the same paths.
+# Dense causal launches split each query block's key walk below these block
+# counts (over all batch entries and heads): the forward between two wave
+# groups below 384 blocks of 256 rows; dQ, below 1024 blocks of 128 rows,
+# between two wave groups or into chunks whose partial sums are added. A
+# split rounds differently, so a prefix run is compared bit for bit with the
+# full run only when its launches take the same paths.
 FWD_SPLIT_BELOW_256 = 384
-DQ_SPLIT_BELOW_128 = 512
+DQ_SPLIT_BELOW_128 = 1024
 
 
 def _prefix_run(run, Lp):
