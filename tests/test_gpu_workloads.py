@@ -40,7 +40,7 @@ from gpu_common import bf16_ulp, check_close, shared_head_allowed, to_f64, to_ho
 pytestmark = pytest.mark.gpu
 
 NAMES = ["gpt1.2b-L32k-fwd", "gpt7b-L131k", "gpt30b-L262k", "L1m", "gqa8-L131k", "gqa2-L131k",
-         "cross-L16k-L131k", "bsparse-L131k"]
+         "cross-L16k-L131k", "bsparse-L131k", "gpt7b-L8k"]
 
 
 def _kv(n):
@@ -405,13 +405,14 @@ _FULL_ONLY_ON_REQUEST = pytest.mark.skipif(
     reason="every element against the fp64 oracle takes minutes of host time; set ULYSSES_FULL_ORACLE=1 to run it")
 
 
-@pytest.mark.parametrize("key", ["gpt1.2b-L32k-fwd",
+@pytest.mark.parametrize("key", ["gpt1.2b-L32k-fwd", "gpt7b-L8k",
                                  pytest.param("gpt7b-L131k", marks=_FULL_ONLY_ON_REQUEST)])
 def test_full_oracle_every_element(key):
     """A workload as the benchmark would run it, every element of rank 0's
     O and LSE (and dQ, dK, dV) against the full fp64 oracle: seconds for the
-    32K forward, about a minute of 16 host cores per head for the 131K
-    forward and backward."""
+    32K forward and the 8K forward and backward (whose launches split every
+    walk: two-group forward, dK/dV halves, dQ chunks), about a minute of 16
+    host cores per head for the 131K forward and backward."""
     run = get_run(key)
     wl = run.wl
     assert run.G == 1

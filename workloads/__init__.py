@@ -134,6 +134,9 @@ WORKLOADS = {
                  block=128, window=16, n_global=1, n_random=2,
                  doc="blocked sparse causal attention, GPT 7B shape (Figs 6-7): 128-token blocks, a window of "
                      "16 blocks, 1 global block and 2 random earlier blocks per block row and head"),
+        Workload("gpt7b-L8k", 9, B=1, L=8192, H=32, d=128, P=8, dtype="bf16", backward=True,
+                 doc="GPT 7B shape at a short context of 8,192 tokens, 4 local heads: launches small "
+                     "enough that every attention kernel splits its walks"),
     ]
 }
 
