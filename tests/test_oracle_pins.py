@@ -699,6 +699,32 @@ def test_block_sparse_matches_torch_masked_sdpa_and_autograd(causal):
     np.testing.assert_allclose(lse, np.log(np.sum(np.where(vis, np.exp(s), 0.0), axis=1)), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_batched_block_sparse_uses_each_heads_layout(causal):
+    """The batched entry points take head h's layout for every batch entry:
+    against torch's fp64 masked attention and autograd on [B, H, L, L] masks
+    built from a different layout per head (a ragged last block included)."""
+    torch = pytest.importorskip("torch")
+    B, L, H, d, block = 2, 88, 3, 8, 16
+    nb = -(-L // block)
+    q, k, v, do = (_rand((B, L, H, d), s) for s in (91, 92, 93, 94))
+    layout = np.stack([_layout(nb, "random", seed=10 + h) for h in range(H)])
+    o, lse = oracle.attn_fwd_block_sparse(q, k, v, layout, block, causal)
+    dq, dk, dv = oracle.attn_bwd_block_sparse(q, k, v, do, layout, block, causal)
+    vis = np.stack([np.kron(layout[h], np.ones((block, block), np.uint8))[:L, :L].astype(bool) for h in range(H)])
+    if causal:
+        vis &= np.tril(np.ones((L, L), bool))[None]
+    mask = torch.from_numpy(np.broadcast_to(vis, (B, H, L, L)).copy())
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    out.backward(torch.from_numpy(np.ascontiguousarray(do.transpose(0, 2, 1, 3))))
+    np.testing.assert_allclose(o, out.detach().numpy().transpose(0, 2, 1, 3), rtol=0, atol=1e-12)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy().transpose(0, 2, 1, 3), rtol=0, atol=1e-11)
+    s = np.einsum("bihe,bjhe->bhij", q, k) / math.sqrt(d)
+    np.testing.assert_allclose(lse, np.log(np.sum(np.where(vis[None], np.exp(s), 0.0), axis=-1)), rtol=0, atol=1e-12)
+
+
 def test_block_sparse_brute_force_and_sampled_rows():
     L, d, block = 40, 5, 8
     q, k, v, do = (_rand((L, d), s) for s in (82, 83, 84, 85))
