@@ -28,8 +28,9 @@
 //   partial sums a reduce kernel adds in chunk order, whichever a cost model
 //   of the launch ranks faster;
 //   dK/dV launches of a few hundred key blocks likewise give each key
-//   block's walk to two workgroups, whose fp32 partial sums the block-layout
-//   reduce kernel adds.
+//   block's walk to two workgroups (causal launches of at most 128 key
+//   blocks: to near-equal parts, more for the longer walks), whose fp32
+//   partial sums the block-layout reduce kernel adds.
 // Grouped-query attention (pinyu.ai, section "Head-count constraints"): a key
 //   head shared by G query heads gets the sum of their gradients; the dK/dV
 //   workgroup walks the query tiles of all G heads in turn and accumulates
@@ -194,15 +195,22 @@ __global__ __launch_bounds__(256) void bwd_sparse_plan_kernel(int ncol, int nlco
 template <int D, bool DENSE = false>
 __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan, int nb, int Lk, int Hk,
                                                                 __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-                                                                float scale, int ndense) {
+                                                                float scale, int ndense, int nkb, int ck) {
   constexpr int UNITS = D / 4, ROWS = 1024 / D;   // units per split column, rows per unit
   const int nunits = (DENSE ? ndense : plan.header[1]) * UNITS;
   const size_t rsk = (size_t)Hk * D;
   for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
     const int sp = u / UNITS;
     const int col = DENSE ? sp : plan.split_col[sp];
-    const int slot = DENSE ? 2 * sp : plan.split_slot[sp];
-    const int nch = DENSE ? 2 : plan.split_nch[sp];
+    int slot = DENSE ? 2 * sp : plan.split_slot[sp];
+    int nch = DENSE ? 2 : plan.split_nch[sp];
+    if (DENSE && ck > 0) {
+      // causal key block kb = nkb - x in ceil(x / ck) parts, numbered as the
+      // dK/dV kernel numbers its work items (nb = batch x K/V heads here)
+      const int x = nkb - col / nb;
+      nch = (x + ck - 1) / ck;
+      slot = nb * (chunk_prefix(nkb, ck) - chunk_prefix(x, ck)) + (col % nb) * nch;
+    }
     const int kb = DENSE ? col / nb : col % nb, hb = DENSE ? col % nb : col / nb;
     const int b = hb / Hk, hk = hb - b * Hk;
     const int row = (u - sp * UNITS) * ROWS + (int)threadIdx.x / (D / 4);   // of [dK | dV][128]
@@ -237,13 +245,15 @@ __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan,
 // (dO) and consumers (Q) share).
 // SPLIT (dense launches of few key blocks): workgroup 2c + h walks half h of
 // key-block column c's query tiles and leaves unscaled fp32 partial sums in
-// slot 2c + h, which the reduce kernel adds in order.
+// slot 2c + h, which the reduce kernel adds in order; with ck > 0 (causal)
+// key block kb is cut into ceil((nkb_all - kb) / ck) parts instead, work
+// item i writing slot i.
 template <int D, bool CAUSAL, bool SPARSE, bool SPLIT = false>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
-    float scale, const uint8_t* __restrict__ layout, int nb, const SparsePlan plan, int nkb_all) {
+    float scale, const uint8_t* __restrict__ layout, int nb, const SparsePlan plan, int nkb_all, int ck) {
   constexpr int BQ = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BQ * CPR / 256, RSTEP = 256 / CPR;
   constexpr int ST = Stride<D>::both;  // Q and dO tiles are read along rows and transposed
   __shared__ __attribute__((aligned(16))) __bf16 Qs[2][BQ * ST];
@@ -273,10 +283,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     slot = it.w;
   }
   if constexpr (SPLIT) {
-    col = (int)blockIdx.x >> 1;
-    chunk = (int)blockIdx.x & 1;
-    nchunk = 2;
-    slot = 2 * col;
+    if (CAUSAL && ck > 0) {
+      // key block kb = nkb_all - x cut into ceil(x / ck) parts, columns
+      // longest first; the items before key block kb number
+      // nhb (S(nkb_all) - S(x)) with S(m) = chunk_prefix(m, ck)
+      const int i = blockIdx.x;
+      const int sn = chunk_prefix(nkb_all, ck);
+      int lo = 1, hi = nkb_all;   // the smallest x whose predecessors number at most i
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (nhb * (sn - chunk_prefix(mid, ck)) <= i)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      nchunk = (lo + ck - 1) / ck;
+      const int loc = i - nhb * (sn - chunk_prefix(lo, ck));
+      const int hbi = loc / nchunk;
+      chunk = loc - hbi * nchunk;
+      col = (nkb_all - lo) * nhb + hbi;
+      slot = i - chunk;
+    } else {
+      col = (int)blockIdx.x >> 1;
+      chunk = (int)blockIdx.x & 1;
+      nchunk = 2;
+      slot = 2 * col;
+    }
   } else if constexpr (!SPARSE) {
     // jobs (key block kb, head pair hb) in order kb * nhb + hb, longest first.
     // Workgroup i runs on XCD i mod 8 (round-robin dispatch); each XCD takes
@@ -307,8 +339,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   int nsteps = G * nqt;
   int tbase = 0;   // first step of this workgroup's share of the walk (SPLIT)
   if constexpr (SPLIT) {
-    tbase = chunk ? nsteps / 2 : 0;
-    nsteps = chunk ? nsteps - nsteps / 2 : nsteps / 2;
+    tbase = chunk * nsteps / nchunk;
+    nsteps = (chunk + 1) * nsteps / nchunk - tbase;
   }
   // under the causal mask only the first two query tiles reach above a key of this block
   const int nmask = CAUSAL ? min(nqt, 2) : 0;
@@ -1006,6 +1038,21 @@ inline bool dkdv_split(const AttnShape& s) {
   return s.causal ? ncol < 512 : ncol <= 128;
 }
 
+// Causal splits of at most 128 columns run all their halves at once, so the
+// half of key block 0 (about G * nkb query tiles) sets the time, twice the
+// average. Such launches cut key block kb instead into ceil((nkb - kb) / t)
+// near-equal parts (at most 2t G tiles each): the smallest t whose parts
+// still fit one round (256 workgroups) and the halves' two slots per column,
+// taken when it shortens the longest item by a fifth or more. 0: halves.
+inline int dkdv_chunk_t(const AttnShape& s) {
+  if (!dkdv_split(s) || !s.causal) return 0;
+  const int64_t nkb = (s.Lk + 127) / 128, nkhb = (int64_t)s.B * s.Hk, ncol = nkb * nkhb;
+  if (2 * ncol > 256) return 0;   // several rounds of halves: longest first already pairs them evenly
+  for (int64_t t = 1; t < nkb; ++t)
+    if (nkhb * chunk_prefix((int)nkb, (int)t) <= 2 * ncol) return 10 * t <= 4 * nkb ? (int)t : 0;
+  return 0;
+}
+
 // Dense dQ launches with few 128-row query blocks W split each block's key
 // walk between two wave groups of one workgroup (as the forward does for
 // small launches), or cut it into chunks (below).
@@ -1126,25 +1173,27 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)(ncol + kSparseSlots)), dim3(512), 0,
                        stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, s.layout, nb, plan,
-                       nkb);
+                       nkb, 0);
     hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D>), dim3(1024), dim3(256), 0, stream, plan, nb, s.Lk, s.Hk,
-                       (__bf16*)dk, (__bf16*)dv, scale, 0);
+                       (__bf16*)dk, (__bf16*)dv, scale, 0, 0, 0);
   } else if (dkdv_split(s)) {
     SparsePlan plan;
     workspace_layout(s, false, &plan, reinterpret_cast<char*>(delta));
     const int ncol = nkb * nkhb;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false, true>), dim3((unsigned)(2 * ncol)), dim3(512), 0,
+    const int ck = dkdv_chunk_t(s);
+    const int items = ck ? nkhb * chunk_prefix(nkb, ck) : 2 * ncol;
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false, true>), dim3((unsigned)items), dim3(512), 0,
                        stream, (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0, plan,
-                       nkb);
+                       nkb, ck);
     hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D, true>), dim3(1024), dim3(256), 0, stream, plan, nkhb, s.Lk,
-                       s.Hk, (__bf16*)dk, (__bf16*)dv, scale, ncol);
+                       s.Hk, (__bf16*)dk, (__bf16*)dv, scale, ncol, nkb, ck);
   } else {
     const unsigned grid = (unsigned)((nkb * nkhb + 255) / 256 * 256);   // whole rounds of 256 jobs
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0,
-                       SparsePlan{}, nkb);
+                       SparsePlan{}, nkb, 0);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -36,3 +36,19 @@ def dq_chunk_items(B, Lq, Lk, Hl, causal):
         if cost < best:
             best, items_best = cost, items
     return items_best
+
+
+def dkdv_chunk_t(B, L, Hk, causal):
+    """Part length t of a balanced dK/dV split (0: halves or no split): causal
+    bf16 launches of at most 128 key-block columns (batch x local K/V heads x
+    128-token key blocks) cut key block kb into ceil((nkb - kb) / t) parts,
+    with the smallest t whose parts fit the halves' two slots per column,
+    taken when 2t is at most 0.8 of nkb."""
+    nkb, nkhb = -(-L // 128), B * Hk
+    ncol = nkb * nkhb
+    if not causal or ncol >= 512 or 2 * ncol > 256:
+        return 0
+    for t in range(1, nkb):
+        if nkhb * chunk_prefix(nkb, t) <= 2 * ncol:
+            return t if 10 * t <= 4 * nkb else 0
+    return 0

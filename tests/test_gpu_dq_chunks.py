@@ -1,12 +1,14 @@
-"""GPU parity of dQ launches that cut their query blocks' key walks into chunks.
+"""GPU parity of backward launches that cut their walks into balanced chunks.
 
 Launches of few 128-row query blocks split every block's walk over its key
 tiles between several workgroups, whose fp32 partial sums a reduce kernel
 adds in chunk order (tests/plans.py restates the plan). Every case below is
 one the host cuts (asserted), with several chunks per block: ragged
 sequence ends, both head dims, grouped-query heads, bidirectional and
-cross-attention. dQ, dK and dV are compared element by element with the fp64
-oracle on the same input bits; a chunked launch is bitwise repeatable.
+cross-attention. Causal dK/dV launches of few key-block columns likewise cut
+key block kb into parts of near-equal length (the last test). dQ, dK and dV
+are compared element by element with the fp64 oracle on the same input bits;
+a chunked launch is bitwise repeatable.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ import oracle
 from workloads import custom, host_tensor
 
 from gpu_common import check_close, shared_head_allowed, to_device, to_f64, to_host_bits, torch_mod
-from plans import dq_chunk_items
+from plans import dkdv_chunk_t, dq_chunk_items
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +61,7 @@ def _run(host, B, Lq, Lk, Hq, Hkv, d, causal):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,d,causal", CASES)
-def test_chunked_dq_matches_oracle(B, Lq, Lk, Hq, Hkv, d, causal):
-    assert dq_chunk_items(B, Lq, Lk, Hq, causal) > 0, "the host no longer cuts this launch"
+def _check_against_oracle(B, Lq, Lk, Hq, Hkv, d, causal):
     host = _inputs(B, Lq, Lk, Hq, Hkv, d)
     dq, dk, dv = _run(host, B, Lq, Lk, Hq, Hkv, d, causal)
     f = {n: oracle.to_f64(host[n], "bf16") for n in host}
@@ -80,6 +80,25 @@ def test_chunked_dq_matches_oracle(B, Lq, Lk, Hq, Hkv, d, causal):
         allowed = {nm: shared_head_allowed(parts[nm], want, "bf16") for nm, want in (("dK", dk_r), ("dV", dv_r))}
     check_close("dK", to_f64(dk, "bf16"), dk_r, "bf16", allowed=allowed["dK"])
     check_close("dV", to_f64(dv, "bf16"), dv_r, "bf16", allowed=allowed["dV"])
+
+
+@pytest.mark.parametrize("B,Lq,Lk,Hq,Hkv,d,causal", CASES)
+def test_chunked_dq_matches_oracle(B, Lq, Lk, Hq, Hkv, d, causal):
+    assert dq_chunk_items(B, Lq, Lk, Hq, causal) > 0, "the host no longer cuts this launch"
+    _check_against_oracle(B, Lq, Lk, Hq, Hkv, d, causal)
+
+
+DKDV_CASES = [  # B, L, Hq, Hkv, d: causal, all with a balanced dK/dV split
+    (1, 2000, 2, 1, 128),     # two query heads per K/V head, ragged end: parts of at most 12 tiles
+    (2, 1500, 2, 2, 64),
+    (1, 4096, 4, 4, 128),     # the 4K x 4 heads shape: 252 parts of at most 22 tiles
+]
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d", DKDV_CASES)
+def test_balanced_dkdv_split_matches_oracle(B, L, Hq, Hkv, d):
+    assert dkdv_chunk_t(B, L, Hkv, True) > 0, "the host no longer cuts this launch"
+    _check_against_oracle(B, L, L, Hq, Hkv, d, True)
 
 
 def test_chunked_dq_is_bitwise_repeatable():
