@@ -101,6 +101,29 @@ def test_balanced_dkdv_split_matches_oracle(B, L, Hq, Hkv, d):
     _check_against_oracle(B, L, L, Hq, Hkv, d, True)
 
 
+def _draw_chunked_case(i):
+    """Seeded shape (seed 9500 + i) that the host cuts: 1.5K-6K tokens, 1-4
+    query heads over 1 or 2 K/V heads, causal or bidirectional, either head
+    dim; redrawn until the dQ launch is chunked."""
+    rng = np.random.default_rng(9500 + i)
+    while True:
+        L = int(rng.integers(1500, 6001))
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 2]))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        if dq_chunk_items(1, L, L, Hq, causal) > 0:
+            return 1, L, L, Hq, Hkv, d, causal
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_chunked_launches_match_oracle(i):
+    B, Lq, Lk, Hq, Hkv, d, causal = _draw_chunked_case(i)
+    print(f"case {i}: B={B} L={Lq} Hq={Hq} Hkv={Hkv} d={d} causal={causal} "
+          f"dQ items={dq_chunk_items(B, Lq, Lk, Hq, causal)} dK/dV t={dkdv_chunk_t(B, Lk, Hkv, causal)}", flush=True)
+    _check_against_oracle(B, Lq, Lk, Hq, Hkv, d, causal)
+
+
 def test_chunked_dq_is_bitwise_repeatable():
     B, Lq, Lk, Hq, Hkv, d, causal = CASES[0]
     host = _inputs(B, Lq, Lk, Hq, Hkv, d)
