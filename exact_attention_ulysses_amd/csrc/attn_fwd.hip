@@ -20,7 +20,8 @@
 //   Dense attention: 8 waves x 32 rows = 256 rows per workgroup in two groups
 //   whose MFMA and softmax phases alternate (attn_fwd_bf16_kernel); launches
 //   of only a few hundred query blocks instead split each 128-row block's key
-//   walk between two wave groups and merge the halves through LDS
+//   walk between two wave groups and merge the halves through LDS, and causal
+//   launches of under 192 blocks each 64-row block's walk between four
 //   (attn_fwd_split_bf16_kernel). Block layouts: 4 waves x 32 rows = 128
 //   rows, the layout's block, walking the active key blocks
 //   (attn_fwd_sparse_bf16_kernel). The single-walk kernels compute every row
@@ -246,19 +247,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_sparse_bf16_kernel(
 // running maximum, sum and O accumulators into its own through LDS. The
 // longest query block's chain of key tiles is half as long as in the
 // single-walk kernels, which is what bounds a causal launch of a few hundred
-// query blocks.
-template <int D, bool CAUSAL>
+// query blocks. NGRP = 4 (causal launches of very few blocks): four groups
+// of two waves share a 64-row block, each over a quarter of its key tiles of
+// 32 keys, in the same LDS (their double-buffered tiles are half as long);
+// group 0 folds in groups 1-3 in order.
+template <int D, bool CAUSAL, int NGRP = 2>
 __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
     float sl2) {
-  constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32;
+  static_assert(NGRP == 2 || NGRP == 4, "two or four wave groups");
+  constexpr int WPG = 8 / NGRP, GT = 64 * WPG;   // waves and threads per group
+  constexpr int BM = 32 * WPG, BN = NGRP == 2 ? 64 : 32, KS = D / 16, DT = D / 32, NC = BN / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int CH = BN * CPR / 256;         // chunks per thread of its group's tile
-  constexpr int RSTEP = 256 / CPR;           // rows between a thread's chunks
+  constexpr int CH = BN * CPR / GT;          // chunks per thread of its group's tile
+  constexpr int RSTEP = GT / CPR;            // rows between a thread's chunks
   constexpr int KST = Stride<D>::row;
   constexpr int VST = Stride<D>::col;
-  constexpr int KBYTES = 2 * 2 * BN * KST * 2, VBYTES = 2 * 2 * BN * VST * 2;
+  constexpr int KBYTES = NGRP * 2 * BN * KST * 2, VBYTES = NGRP * 2 * BN * VST * 2;
   // [group][buffer] K and V tiles; reused for the merge once the walks are done
   __shared__ __attribute__((aligned(16))) char smem[KBYTES + VBYTES];
   typedef __bf16 KTile[BN * KST];
@@ -268,13 +274,13 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
   // merge record of one wave of group 1: DT * 16 O values, the running
   // maximum and the partial sum, each as [value][lane]
   constexpr int MREC = (DT * 16 + 2) * 64;
-  static_assert(4 * MREC * 4 <= KBYTES + VBYTES, "merge records exceed the tile buffers");
+  static_assert((NGRP - 1) * WPG * MREC * 4 <= KBYTES + VBYTES, "merge records exceed the tile buffers");
   float* mbuf = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wq = wave & 3;
-  const int gtid = tid & 255;                // thread index within the group
+  const int grp = wave / WPG, wq = wave % WPG;
+  const int gtid = tid % GT;                 // thread index within the group
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / nhb;        // longest rows first
   const int hb = bid % nhb;
@@ -304,10 +310,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
   // diagonal tiles under the causal mask, and one tile more when n is odd
   const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int n = (kend + BN - 1) / BN;
-  const int half = n / 2;
-  const int t0 = grp ? half : 0;
-  const int cnt = grp ? n - half : half;
-  const int steps = n - half;                // both groups pass this many barriers
+  const int t0 = grp * n / NGRP;
+  const int cnt = (grp + 1) * n / NGRP - t0;
+  const int steps = (n + NGRP - 1) / NGRP;   // every group passes this many barriers
 
   const int srow = gtid / CPR, scol = (gtid % CPR) * 8;
   const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
@@ -345,19 +350,19 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       s0 = mfma32(frag_row<KST>(Kc, 0, 16 * ks, lane), qf[ks], s0);
-      s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
+      if constexpr (BN == 64) s1 = mfma32(frag_row<KST>(Kc, 32, 16 * ks, lane), qf[ks], s1);
     }
     if (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk)) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * hl + (e & 3);
         if (CAUSAL ? (key > qrow) : (key >= Lk)) s0[e] = -INFINITY;
-        if (CAUSAL ? (key + 32 > qrow) : (key + 32 >= Lk)) s1[e] = -INFINITY;
+        if (BN == 64 && (CAUSAL ? (key + 32 > qrow) : (key + 32 >= Lk))) s1[e] = -INFINITY;
       }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, BN == 64 ? fmaxf(s0[e], s1[e]) : s0[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mcand = mx * sl2;
     if (__ballot(mcand > m_run + 8.f)) {
@@ -373,9 +378,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
     // diagonal tile before any visible one
     const float nm = m_run == -INFINITY ? 0.f : -m_run;
     float rsum = 0.f;
-    bf16x8 pf[4];
+    bf16x8 pf[NC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float x = (c < 2) ? s0[8 * (c & 1) + i] : s1[8 * (c & 1) + i];
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
     }
     l_run += rsum;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(frag_col<VST>(Vc, 16 * c, 32 * dt, lane), pf[c], oacc[dt]);
     }
@@ -410,8 +415,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
 
   // every tile read ended at the last barrier: group 1 leaves its state in
   // the tile buffers, group 0 folds it into its own
-  float* rec = mbuf + wq * MREC;
-  if (grp == 1) {
+  if (grp > 0) {
+    float* rec = mbuf + ((grp - 1) * WPG + wq) * MREC;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -421,18 +426,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
     rec[(DT * 16 + 1) * 64 + lane] = l_run;
   }
   __syncthreads();
-  if (grp == 1) return;
-  const float m1 = rec[DT * 16 * 64 + lane];
-  const float l1 = rec[(DT * 16 + 1) * 64 + lane];
-  const float m = fmaxf(m_run, m1);
-  const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-  const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+  if (grp > 0) return;
+  // group 0 folds in groups 1 .. NGRP-1 in order
+  for (int g = 1; g < NGRP; ++g) {
+    const float* rec = mbuf + ((g - 1) * WPG + wq) * MREC;
+    const float m1 = rec[DT * 16 * 64 + lane];
+    const float l1 = rec[(DT * 16 + 1) * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[dt][e] = oacc[dt][e] * a0 + rec[(dt * 16 + e) * 64 + lane] * a1;
+      for (int e = 0; e < 16; ++e) oacc[dt][e] = oacc[dt][e] * a0 + rec[(dt * 16 + e) * 64 + lane] * a1;
+    }
+    l_run = l_run * a0 + l1 * a1;
+    m_run = m;
   }
-  l_run = l_run * a0 + l1 * a1;
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(oacc[dt], a, inv);
     }
-    if (hl == 0) lse[(size_t)hb * Lq + qrow] = l_tot > 0.f ? (m + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (hl == 0) lse[(size_t)hb * Lq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 
@@ -707,6 +717,12 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
 // workgroup count still fits the 256 CUs at once (W = 128: +50 %).
 constexpr int64_t kSplitCausalBelow = 384;
 constexpr int64_t kSplitFullUpTo = 128;
+// Causal launches of fewer than 192 such blocks (the longest walk then twice
+// the average or more even when split in two) give each 64-row block to four
+// groups of two waves over 32-key tiles instead: twice the workgroups, half
+// the longest walk, at half the MFMA work per barrier (measured: 64 blocks
+// -18 to -25 %, 128 blocks -15 %; at 256 blocks two groups are 25 % faster).
+constexpr int64_t kSplit4CausalBelow = 192;
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnShape& s,
@@ -722,7 +738,12 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   else {
     const int nqb2 = (s.Lq + 255) / 256;
     const int64_t W = (int64_t)nqb2 * nhb;
-    if (CAUSAL ? W < kSplitCausalBelow : W <= kSplitFullUpTo)
+    if (CAUSAL && W < kSplit4CausalBelow) {
+      const int nqb64 = (s.Lq + 63) / 64;
+      hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nqb64 * nhb), dim3(512), 0, stream,
+                         (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
+                         s.Hk, s.Hq / s.Hk, nqb64, nhb, sl2);
+    } else if (CAUSAL ? W < kSplitCausalBelow : W <= kSplitFullUpTo)
       hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(512), 0, stream,
                          (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
                          s.Hk, s.Hq / s.Hk, nqb, nhb, sl2);

@@ -228,11 +228,13 @@ def test_forward_sampled_rows(key):
 
 # Dense causal launches split each query block's key walk below these block
 # counts (over all batch entries and heads): the forward between two wave
-# groups below 384 blocks of 256 rows; dQ, below 1024 blocks of 128 rows,
-# between two wave groups or into chunks whose partial sums are added. A
-# split rounds differently, so a prefix run is compared bit for bit with the
-# full run only when its launches take the same paths.
+# groups below 384 blocks of 256 rows and between four below 192; dQ, below
+# 1024 blocks of 128 rows, between two wave groups or into chunks whose
+# partial sums are added. A split rounds differently, so a prefix run is
+# compared bit for bit with the full run only when its launches take the
+# same paths.
 FWD_SPLIT_BELOW_256 = 384
+FWD_SPLIT4_BELOW_256 = 192
 DQ_SPLIT_BELOW_128 = 1024
 
 
@@ -271,13 +273,17 @@ def _prefix_run(run, Lp):
 
 def _same_path_prefix(wl):
     """Shortest prefix length >= PREFIX whose dense launches take the full run's paths
-    (splitting is monotone: a launch below a threshold splits, and so does any shorter one)."""
+    (each path covers a range of launch sizes: at least the lower end of the full
+    run's range keeps the prefix on it)."""
     if wl.block:
         return PREFIX
     nhb = wl.B * wl.Hp
     Lb = PREFIX
-    if -(-wl.L // 256) * nhb >= FWD_SPLIT_BELOW_256:
+    w256 = -(-wl.L // 256) * nhb
+    if w256 >= FWD_SPLIT_BELOW_256:
         Lb = max(Lb, -(-FWD_SPLIT_BELOW_256 // nhb) * 256)
+    elif w256 >= FWD_SPLIT4_BELOW_256:
+        Lb = max(Lb, -(-FWD_SPLIT4_BELOW_256 // nhb) * 256)
     if wl.backward and -(-wl.L // 128) * nhb >= DQ_SPLIT_BELOW_128:
         Lb = max(Lb, -(-DQ_SPLIT_BELOW_128 // nhb) * 128)
     return min(wl.L, -(-Lb // 256) * 256)
