@@ -20,8 +20,8 @@
 //   Dense attention: 8 waves x 32 rows = 256 rows per workgroup in two groups
 //   whose MFMA and softmax phases alternate (attn_fwd_bf16_kernel); launches
 //   of only a few hundred query blocks instead split each 128-row block's key
-//   walk between two wave groups and merge the halves through LDS, and causal
-//   launches of under 192 blocks each 64-row block's walk between four
+//   walk between two wave groups and merge the halves through LDS, and the
+//   smallest launches each 64-row block's walk between four
 //   (attn_fwd_split_bf16_kernel). Block layouts: 4 waves x 32 rows = 128
 //   rows, the layout's block, walking the active key blocks
 //   (attn_fwd_sparse_bf16_kernel). The single-walk kernels compute every row
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_sparse_bf16_kernel(
 // running maximum, sum and O accumulators into its own through LDS. The
 // longest query block's chain of key tiles is half as long as in the
 // single-walk kernels, which is what bounds a causal launch of a few hundred
-// query blocks. NGRP = 4 (causal launches of very few blocks): four groups
+// query blocks. NGRP = 4 (launches of very few blocks): four groups
 // of two waves share a 64-row block, each over a quarter of its key tiles of
 // 32 keys, in the same LDS (their double-buffered tiles are half as long);
 // group 0 folds in groups 1-3 in order.
@@ -722,7 +722,11 @@ constexpr int64_t kSplitFullUpTo = 128;
 // groups of two waves over 32-key tiles instead: twice the workgroups, half
 // the longest walk, at half the MFMA work per barrier (measured: 64 blocks
 // -18 to -25 %, 128 blocks -15 %; at 256 blocks two groups are 25 % faster).
+// Bidirectional launches of at most 64 blocks, which two groups leave on half
+// the CUs, likewise (-20 to -23 %; at 128 blocks two groups fill the chip and
+// are 25 % faster).
 constexpr int64_t kSplit4CausalBelow = 192;
+constexpr int64_t kSplit4FullUpTo = 64;
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const AttnShape& s,
@@ -738,7 +742,7 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
   else {
     const int nqb2 = (s.Lq + 255) / 256;
     const int64_t W = (int64_t)nqb2 * nhb;
-    if (CAUSAL && W < kSplit4CausalBelow) {
+    if (CAUSAL ? W < kSplit4CausalBelow : W <= kSplit4FullUpTo) {
       const int nqb64 = (s.Lq + 63) / 64;
       hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nqb64 * nhb), dim3(512), 0, stream,
                          (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
