@@ -52,3 +52,16 @@ def dkdv_chunk_t(B, L, Hk, causal):
         if nkhb * chunk_prefix(nkb, t) <= 2 * ncol:
             return t if 10 * t <= 4 * nkb else 0
     return 0
+
+
+def fwd_groups(B, Lq, Hq, causal):
+    """Wave groups that share each query block's key walk in a dense bf16
+    forward launch of W = ceil(Lq / 256) x B x Hq blocks: four below 192 causal
+    blocks or up to 64 bidirectional ones, two below 384 causal or up to 128
+    bidirectional ones, else one walk per block."""
+    W = -(-Lq // 256) * B * Hq
+    if W < 192 if causal else W <= 64:
+        return 4
+    if W < 384 if causal else W <= 128:
+        return 2
+    return 1

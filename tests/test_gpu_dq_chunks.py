@@ -8,7 +8,9 @@ sequence ends, both head dims, grouped-query heads, bidirectional and
 cross-attention. Causal dK/dV launches of few key-block columns likewise cut
 key block kb into parts of near-equal length (the last test). dQ, dK and dV
 are compared element by element with the fp64 oracle on the same input bits;
-a chunked launch is bitwise repeatable.
+a chunked launch is bitwise repeatable. The forward of the smallest launches
+shares each 64-row block's key walk among four wave groups; its O and LSE
+are checked the same way.
 """
 import numpy as np
 import pytest
@@ -17,8 +19,8 @@ import exact_attention_ulysses_amd as U
 import oracle
 from workloads import custom, host_tensor
 
-from gpu_common import check_close, shared_head_allowed, to_device, to_f64, to_host_bits, torch_mod
-from plans import dkdv_chunk_t, dq_chunk_items
+from gpu_common import LSE_ABS, check_close, shared_head_allowed, to_device, to_f64, to_host_bits, torch_mod
+from plans import dkdv_chunk_t, dq_chunk_items, fwd_groups
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +124,29 @@ def test_random_chunked_launches_match_oracle(i):
     print(f"case {i}: B={B} L={Lq} Hq={Hq} Hkv={Hkv} d={d} causal={causal} "
           f"dQ items={dq_chunk_items(B, Lq, Lk, Hq, causal)} dK/dV t={dkdv_chunk_t(B, Lk, Hkv, causal)}", flush=True)
     _check_against_oracle(B, Lq, Lk, Hq, Hkv, d, causal)
+
+
+FWD4_CASES = [  # B, L, Hq, Hkv, d, causal: launches the forward splits among four wave groups
+    (1, 4096, 4, 4, 128, True),
+    (1, 2000, 4, 2, 128, True),      # grouped-query, ragged end
+    (2, 3000, 2, 2, 64, False),
+    (1, 100, 1, 1, 128, True),       # groups left without key tiles
+]
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,d,causal", FWD4_CASES)
+def test_four_group_forward_matches_oracle(B, L, Hq, Hkv, d, causal):
+    assert fwd_groups(B, L, Hq, causal) == 4, "the host no longer uses four groups here"
+    torch = torch_mod()
+    host = _inputs(B, L, L, Hq, Hkv, d)
+    q, k, v = (to_device(host[n], "bf16") for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    U.ulysses_attn_fwd_gqa(q, k, v, o, lse, B, L, L, Hq, Hkv, d, 1, causal)
+    f = {n: oracle.to_f64(host[n], "bf16") for n in ("q", "k", "v")}
+    o_r, lse_r = oracle.attn_fwd_gqa(f["q"], f["k"], f["v"], causal)
+    check_close("O", to_f64(o, "bf16"), o_r, "bf16")
+    assert np.max(np.abs(lse.cpu().numpy() - lse_r)) <= LSE_ABS["bf16"]
 
 
 def test_chunked_dq_is_bitwise_repeatable():
