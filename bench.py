@@ -142,6 +142,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
                     help="prefix length of one head that the fp64 oracle runs fwd+bwd on")
+    ap.add_argument("--cold-reps", type=int, default=3,
+                    help="repetitions of each layout change timed after a cache-evicting write")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 runs)")
     ap.add_argument("--gemm-ceiling", action="store_true",
@@ -162,8 +164,17 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, seq_host, tokens: int, layout=None):
-    """Time the fp64 oracle (as it stands) on a bounded sample of the workload."""
+def cpu_baseline(wl, prefix_host, layout=None):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload.
+
+    prefix_host holds the raw bits of the first T tokens of each input (B = 1:
+    the first T token rows of the global [L][H][d_h] tensor are the seq
+    buffer of the same problem at length T). The oracle runs its own
+    seq_to_head over all P ranks of that T-token problem, then attention
+    forward (and backward) of head 0 of rank 0 over the T tokens. Its rates
+    also give an extrapolated time for the whole step at full size: attention
+    work grows as the visible pairs, the layout changes as the bytes.
+    """
     import numpy as np
     import oracle
     try:
@@ -172,42 +183,60 @@ def cpu_baseline(wl, seq_host, tokens: int, layout=None):
     except Exception:  # pragma: no cover
         threads = None
     cores = len(os.sched_getaffinity(0))
-    B, L, H, d, P = wl.B, wl.L, wl.H, wl.d, wl.P
-    Ls, Lks = min(tokens, L), min(tokens, wl.Lk)
+    B, d, P = wl.B, wl.d, wl.P
+    assert B == 1
+    T = prefix_host["q"].size // (wl.H * d)
+    Tk = prefix_host["k"].size // (wl.Hk * d)
     t0 = time.perf_counter()
     heads, perm_bytes = {}, 0
-    for n, x in seq_host.items():
+    for n, x in prefix_host.items():
         if n in ("k", "v"):
-            heads[n] = oracle.seq_to_head_kv(x, B, wl.Lk, wl.Hk, d, P)[0]
-            perm_bytes += x.nbytes // P + heads[n].nbytes     # rank 0's share of the reads, its block written
+            xh = oracle.seq_to_head_kv(x, B, Tk, wl.Hk, d, P)
         else:
-            heads[n] = oracle.seq_to_head_part(x, B, L, H, d, P, 0)
-            perm_bytes += 2 * x.nbytes // P
+            xh = oracle.seq_to_head(x, B, T, wl.H, d, P)
+        perm_bytes += x.nbytes + xh.nbytes      # read once, written once
+        heads[n] = xh[0]
     t_perm = time.perf_counter() - t0
-    f = {n: oracle.to_f64(heads[n][0, :(Lks if n in ("k", "v") else Ls), 0], wl.dtype) for n in heads}
+    f = {n: oracle.to_f64(heads[n][0, :, 0], wl.dtype) for n in heads}
     t0 = time.perf_counter()
+    gemms = 6 if wl.backward else 2          # the oracle's products: S, PV (+ dP, dV, dQ, dK), no recompute
     if layout is not None:    # block-sparse: the layout of head 0 over the sampled prefix
-        nbs = -(-Ls // wl.block)
+        nbs = -(-T // wl.block)
         lay = layout[0, :nbs, :nbs]
         if wl.backward:
             oracle.attn_bwd_block_sparse_head(f["q"], f["k"], f["v"], f["do"], lay, wl.block, wl.causal)
         else:
             oracle.attn_fwd_block_sparse_head(f["q"], f["k"], f["v"], lay, wl.block, wl.causal)
-        flops = (14 if wl.backward else 4) * d * npairs_layout(lay[None], wl.block, Ls, wl.causal)
-    elif wl.backward:
-        oracle.attn_bwd_head(f["q"], f["k"], f["v"], f["do"], wl.causal)
-        flops = 14 * d * npairs(Ls, wl.causal, Lks)
+        pairs = npairs_layout(lay[None], wl.block, T, wl.causal)
+        full_pairs = None
     else:
-        oracle.attn_fwd_head(f["q"], f["k"], f["v"], wl.causal)
-        flops = 4 * d * npairs(Ls, wl.causal, Lks)
+        if wl.backward:
+            oracle.attn_bwd_head(f["q"], f["k"], f["v"], f["do"], wl.causal)
+        else:
+            oracle.attn_fwd_head(f["q"], f["k"], f["v"], wl.causal)
+        pairs = npairs(T, wl.causal, Tk)
+        full_pairs = wl.B * wl.Hp * npairs(wl.L, wl.causal, wl.Lk)
     t_attn = time.perf_counter() - t0
-    return {"value": flops / t_attn / 1e12, "unit": "TFLOP/s", "cores": threads if threads else cores,
-            "host_cores_visible": cores, "cpu_model": _cpu_model(), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, {'fwd+bwd' if wl.backward else 'fwd'} of head 0 of rank 0 over the "
-                       f"first {Ls} query and {Lks} key tokens of the same inputs ({t_attn:.1f} s); flops "
-                       f"counted as on the GPU"),
-            "perm_GBps": perm_bytes / t_perm / 1e9,
-            "perm_sample": f"seq_to_head of rank 0's share of {len(seq_host)} tensors ({t_perm:.1f} s)"}
+    flops = 2 * gemms * d * pairs
+    rate = flops / t_attn
+    perm_rate = perm_bytes / t_perm
+    out = {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads if threads else cores,
+           "host_cores_visible": cores, "cpu_model": _cpu_model(), "kind": "oracle",
+           "sample": (f"fp64 numpy oracle: seq_to_head over all {P} ranks of the first {T} tokens of "
+                      f"{len(prefix_host)} inputs ({t_perm:.1f} s), then attention "
+                      f"{'fwd+bwd' if wl.backward else 'fwd'} of head 0 of rank 0 over those {T} tokens "
+                      f"({t_attn:.1f} s)"),
+           "flops_counted": f"{2 * gemms}*d_h*Npairs (the oracle's {gemms} products, no recompute)",
+           "attn_s": t_attn, "perm_s": t_perm, "perm_GBps": perm_rate / 1e9}
+    if full_pairs is not None:
+        n_perm = 2 * len(prefix_host)       # every input in, every output back
+        full_perm_bytes = n_perm * 2 * wl.tensor_bytes
+        est = 2 * gemms * d * full_pairs / rate + full_perm_bytes / perm_rate
+        out["extrapolated_full_s"] = est
+        out["extrapolated_full_note"] = (f"extrapolated, not run: one step at full size ({wl.L} tokens, "
+                                         f"{wl.B * wl.Hp} heads, {n_perm} layout changes of "
+                                         f"{wl.tensor_bytes / 1e9:.2f} GB) at the sampled rates")
+    return out
 
 
 def gemm_ceiling() -> None:
@@ -388,6 +417,37 @@ def main():
         detail.update({"attn_bwd_ms": avg["attn_bwd"],
                        "attn_bwd_TFLOPs": bwd_flops / (avg["attn_bwd"] * 1e-3) / 1e12})
 
+    # Layout changes timed cold: a 1 GiB write before every repetition evicts
+    # the 256 MB last-level cache (and the L2) so no tensor is timed from
+    # cache; the write is outside the events.
+    evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = {}
+    for name, fn, nbytes in ops:
+        if name not in ("seq_to_head", "head_to_seq"):
+            continue
+        for _ in range(args.cold_reps):
+            evict.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            cold.setdefault(name, []).append((e0.elapsed_time(e1), nbytes))
+    del evict
+    cold_ms = {k: sum(t for t, _ in v) / len(v) for k, v in cold.items()}
+    cold_gbps = {k: sum(b for _, b in v) / (sum(t for t, _ in v) * 1e-3) / 1e9 for k, v in cold.items()}
+    all_cold = [x for v in cold.values() for x in v]
+    detail.update({"seq_to_head_ms_cold": cold_ms.get("seq_to_head"), "head_to_seq_ms_cold": cold_ms.get("head_to_seq"),
+                   "seq_to_head_GBps_cold": cold_gbps.get("seq_to_head"),
+                   "head_to_seq_GBps_cold": cold_gbps.get("head_to_seq"),
+                   "transpose_GBps_cold": sum(b for _, b in all_cold) / (sum(t for t, _ in all_cold) * 1e-3) / 1e9,
+                   "transpose_cold_note": f"{args.cold_reps} reps of every layout change, each after a 1 GiB "
+                                          "cache-evicting write outside the events"})
+    detail["transpose_frac_peak_cold"] = detail["transpose_GBps_cold"] / PEAK_HBM_GBPS
+    for nm in ("seq_to_head", "head_to_seq"):     # in the timed steps: bytes per step over time per step
+        detail[nm + "_GBps"] = (sum(b for n_, _, b in ops if n_ == nm) / 1e9
+                                / (sum(per_op[nm]) / args.steps * 1e-3)) if nm in per_op else None
+
     if args.calibration_copy:
         src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -397,8 +457,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        host = {n: seq[n].view(torch.int16).cpu().numpy().view("uint16") for n in ins}
-        cpu = cpu_baseline(wl, host, args.cpu_sample_tokens, layout_host)
+        # only the sampled prefix crosses to the host: the first T tokens (a
+        # multiple of P) of every input
+        T = max(P, min(args.cpu_sample_tokens, L) // P * P)
+        Tk = max(P, min(args.cpu_sample_tokens, Lk) // P * P)
+        host = {n: seq[n].view(-1)[:(Tk * Hk if kv(n) else T * H) * d].view(torch.int16).cpu().numpy().view("uint16")
+                for n in ins}
+        cpu = cpu_baseline(wl, host, layout_host)
 
     metric = METRIC if wl.key == HEADLINE else METRIC.replace(
         "causal attn", ("causal" if causal else "bidirectional") + (" block-sparse" if wl.block else "")

@@ -233,27 +233,32 @@ def attn_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool = True,
 # exact attention, backward (explicit formula, fp64)
 # ---------------------------------------------------------------------------
 
-def attn_bwd_head(q, k, v, do, causal: bool, row_block: int = ROW_BLOCK):
+def attn_bwd_head(q, k, v, do, causal: bool, row_block: int = ROW_BLOCK,
+                  rows: Optional[Tuple[int, int]] = None):
     """One head: the exact gradient of <dO, O> w.r.t. q, k, v (float64; q, do
     [Lq, d], k, v [Lkv, d]).
 
     Per row block the probabilities are formed once and used for O, D, dP,
     dS and the three products; dK and dV accumulate over the row blocks.
-    Returns (dq, dk, dv, o, lse, D).
+    Returns (dq, dk, dv, o, lse, D). With rows = (r0, r1) only query rows
+    r0 <= i < r1 are processed: their dq, o, lse and D are filled (the other
+    rows stay 0), and dk, dv hold those rows' terms alone, so the dk, dv of
+    a partition of the rows add up to the whole.
     """
     L, d = q.shape
     Lkv = k.shape[0]
     if causal and Lkv != L:
         raise ValueError("causal attention needs Lq == Lkv")
     scale = 1.0 / math.sqrt(d)
+    r0, r1 = (0, L) if rows is None else (max(0, int(rows[0])), min(L, int(rows[1])))
     dq = np.zeros((L, d))
     dk = np.zeros((Lkv, d))
     dv = np.zeros((Lkv, d))
-    o = np.empty((L, d))
-    lse = np.empty((L,))
-    D = np.empty((L,))
-    for i0 in range(0, L, row_block):
-        i1 = min(L, i0 + row_block)
+    o = np.zeros((L, d))
+    lse = np.zeros((L,))
+    D = np.zeros((L,))
+    for i0 in range(r0, r1, row_block):
+        i1 = min(r1, i0 + row_block)
         nk = _visible_keys(i1, Lkv, causal)
         s = _scores(q[i0:i1], k[:nk], i0, causal, scale)
         p, lse[i0:i1] = _softmax_rows(s)
@@ -621,14 +626,16 @@ def attn_rows(q, k, v, rows: Sequence[int], causal: bool = True, do=None):
 
 
 def attn_dkv_cols(q, k, v, do, cols: Sequence[int], causal: bool = True,
-                  row_block: int = ROW_BLOCK):
+                  row_block: int = ROW_BLOCK, rows: Optional[Tuple[int, int]] = None):
     """dK and dV of selected key columns j of one head.
 
     dK_j = (1/sqrt d) sum_{i sees j} dS_ij q_i and dV_j = sum_{i sees j} P_ij dO_i.
     Every row i that sees some selected column needs its own LSE_i and D_i,
     which are formed here from the full row (no value comes from elsewhere).
     Cost O(#rows-that-see-the-columns * L * d); cheap for columns near the end
-    of a causal sequence.
+    of a causal sequence. With rows = (r0, r1) only the terms of query rows
+    r0 <= i < r1 are summed, so the sums of a partition of the rows add up to
+    the whole (callers may form the parts concurrently).
     """
     Lk, d = k.shape
     Lq = q.shape[0]
@@ -636,13 +643,14 @@ def attn_dkv_cols(q, k, v, do, cols: Sequence[int], causal: bool = True,
         raise ValueError("causal attention needs Lq == Lkv")
     scale = 1.0 / math.sqrt(d)
     cols = np.asarray(sorted(set(int(c) for c in cols)), dtype=np.int64)
-    first_row = int(cols.min()) if causal else 0
+    r0, r1 = (0, Lq) if rows is None else (max(0, int(rows[0])), min(Lq, int(rows[1])))
+    first_row = max(r0, int(cols.min())) if causal else r0
     dk = np.zeros((len(cols), d))
     dv = np.zeros((len(cols), d))
     kc = np.asarray(k[cols], dtype=np.float64)
     vc = np.asarray(v[cols], dtype=np.float64)
-    for i0 in range(first_row, Lq, row_block):
-        i1 = min(Lq, i0 + row_block)
+    for i0 in range(first_row, r1, row_block):
+        i1 = min(r1, i0 + row_block)
         nk = _visible_keys(i1, Lk, causal)
         qb = np.asarray(q[i0:i1], dtype=np.float64)
         dob = np.asarray(do[i0:i1], dtype=np.float64)

@@ -1,4 +1,7 @@
 """Shared helpers of the GPU parity tests (host side only)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 import oracle
@@ -42,6 +45,10 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 8)
 
 
+# every comparison check_close made in this process, for the end-of-run summary
+RECORDS = []
+
+
 def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, allowed=None, abs_sum=None):
     """Compare a kernel output with the fp64 oracle value `want`.
 
@@ -56,17 +63,27 @@ def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, al
     adds 2^-8 * abs_sum to the elementwise bar: the bound on rounding the
     probabilities (or dS) to bf16 before they enter the products, from the
     oracle's absolute sums (oracle.attn_abs_sums_head).
+
+    The returned stats always carry the raw figures beside the verdict:
+    max_abs (against the flat 1e-2), n_over_flat (elements more than 1e-2
+    off), and for bf16 max_err_over_unwidened (the worst error over
+    max(1e-2, ulp) alone) next to max_err_over_allowed (over the bar the
+    test applied, widened by `allowed` or `abs_sum` where given).
     """
     st = oracle.error_stats(got, want)
+    err = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(want, dtype=np.float64))
+    st["n"] = int(err.size)
     if dtype == "bf16":
         ma = BF16_MAX_ABS if max_abs is None else max_abs
         rf = BF16_REL_FRO if rel_fro is None else rel_fro
-        err = np.abs(np.asarray(got, dtype=np.float64) - want)
+        plain = np.maximum(ma, bf16_ulp(want))
         if allowed is None:
-            allowed = np.maximum(ma, bf16_ulp(want))
+            allowed = plain
         if abs_sum is not None:
             allowed = allowed + 2.0 ** -8 * np.asarray(abs_sum, dtype=np.float64)
         st["max_err_over_allowed"] = float(np.max(err / allowed)) if err.size else 0.0
+        st["max_err_over_unwidened"] = float(np.max(err / plain)) if err.size else 0.0
+        st["n_over_flat"] = int(np.count_nonzero(err > ma))
         ok = st["max_err_over_allowed"] <= 1.0 and (st["rel_fro"] <= rf or not fro)
     else:
         ma = FP32_MAX_ABS if max_abs is None else max_abs
@@ -74,6 +91,7 @@ def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, al
             ok = st["max_abs"] <= ma
         else:
             ok = bool(np.all(np.abs(np.asarray(got, dtype=np.float64) - want) <= allowed))
+    RECORDS.append((name, dtype, st))
     assert ok, f"{name}: {st} exceeds the {dtype} bar"
     return st
 
@@ -92,3 +110,40 @@ def shared_head_allowed(parts, want, dtype):
     if dtype == "bf16":
         return np.sum(np.maximum(BF16_MAX_ABS, bf16_ulp(parts)), axis=0) + bf16_ulp(want)
     return parts.shape[0] * FP32_MAX_ABS + 2.0 ** -23 * np.abs(want)
+
+
+def host_cores() -> int:
+    """Host threads this process may use (the machine's CPU share when OMP_NUM_THREADS states it)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
+
+
+def host_parallel(fn, items, max_workers=16):
+    """fn over items in host threads (numpy's loops release the interpreter
+    lock, so oracle calls on independent heads or row ranges run side by
+    side). Results in order. BLAS runs one thread per worker: concurrent
+    calls into a multithreaded OpenBLAS from several threads were measured
+    to return wrong products (an fp64 dK off by 1.8e-3 on a 32K-token head),
+    while one BLAS thread per calling thread gave results bit-identical to a
+    sequential run."""
+    from threadpoolctl import threadpool_limits
+    items = list(items)
+    workers = max(1, min(len(items), max_workers, host_cores()))
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, items))
+
+
+def causal_row_ranges(L, parts, block=256):
+    """Cut rows 0..L-1 into `parts` ranges of about equal causal work (row i
+    costs ~i), at multiples of `block`."""
+    cuts = [0]
+    for p in range(1, parts):
+        c = int(round(L * (p / parts) ** 0.5 / block)) * block
+        cuts.append(min(L, max(cuts[-1], c)))
+    cuts.append(L)
+    return [(a, b) for a, b in zip(cuts[:-1], cuts[1:]) if b > a]

@@ -62,3 +62,26 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("backward", [True, False])
+def test_cpu_baseline_on_a_prefix(bench, backward):
+    """The oracle leg runs on the first T tokens only; it counts the oracle's own
+    products (6 with a backward pass, 2 without) and extrapolates a full step."""
+    from workloads import custom, host_tensor
+    wl = custom(1, 512, 8, 64, 4, dtype="bf16", backward=backward, index=950)
+    T = 128
+    names = ["q", "k", "v"] + (["do"] if backward else [])
+    prefix = {n: host_tensor(wl, n).reshape(-1)[:T * wl.H * wl.d] for n in names}
+    r = bench.cpu_baseline(wl, prefix)
+    gemms = 6 if backward else 2
+    flops = 2 * gemms * wl.d * T * (T + 1) // 2
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] == pytest.approx(flops / r["attn_s"] / 1e12)
+    assert f"first {T} tokens" in r["sample"]
+    perm_bytes = 2 * len(names) * T * wl.H * wl.d * 2
+    assert r["perm_GBps"] == pytest.approx(perm_bytes / r["perm_s"] / 1e9)
+    full = 2 * gemms * wl.d * wl.Hp * wl.L * (wl.L + 1) // 2 / (flops / r["attn_s"]) \
+        + 2 * len(names) * 2 * wl.tensor_bytes / (perm_bytes / r["perm_s"])
+    assert r["extrapolated_full_s"] == pytest.approx(full)
+    assert "extrapolated" in r["extrapolated_full_note"]

@@ -14,8 +14,11 @@ output):
     (for an L' whose launch takes the full run's path), and a run on the
     first 8192 tokens is checked in full against the oracle;
   * backward: dQ of the sampled rows (also prefix-checked), dK/dV of sampled
-    key columns near the end, and over the full outputs the identities
-    sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i.
+    key columns near the end, every element of the early key columns (the
+    longest sums) of the 262K workload's first head, and over the full
+    outputs the identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i;
+  * every element of rank 0's outputs against the full oracle on the 32K
+    forward, the 8K forward and backward and the 131K forward and backward.
 Grouped-query workloads run K and V through the K/V layout change (and dK,
 dV through its gradient form); a K/V head's dK/dV columns are checked
 against the sum of its query heads' oracle columns. The cross-attention
@@ -25,7 +28,6 @@ block-sparse workload runs the block-sparse entry points with rank 0's seeded
 block layout, and every oracle value is formed under the same layout.
 """
 import gc
-import os
 import time
 
 import numpy as np
@@ -35,7 +37,8 @@ import exact_attention_ulysses_amd as U
 import oracle
 from workloads import WORKLOADS, block_layout, device_tensor, stress_positions
 
-from gpu_common import bf16_ulp, check_close, shared_head_allowed, to_f64, to_host_bits, torch_mod
+from gpu_common import (bf16_ulp, causal_row_ranges, check_close, host_parallel, shared_head_allowed, to_f64,
+                        to_host_bits, torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -406,19 +409,45 @@ def test_backward_identities_over_full_outputs(key):
         assert np.all(np.abs(sk) <= bound_k), (j, np.max(np.abs(sk) / bound_k))
 
 
-_FULL_ONLY_ON_REQUEST = pytest.mark.skipif(
-    not os.environ.get("ULYSSES_FULL_ORACLE"),
-    reason="every element against the fp64 oracle takes minutes of host time; set ULYSSES_FULL_ORACLE=1 to run it")
+@pytest.mark.parametrize("key", ["gpt30b-L262k"])
+def test_backward_early_key_columns(key):
+    """dK and dV of the early key columns at full size, every element of them:
+    key 0 is seen by every query row, so these are the longest sums of the
+    backward and the first work items of the dK/dV launch, plus the tile
+    edges 63/64 and 127/128, the middle key, and the stressed K row of the
+    head. Each column needs every later row's LSE and D, so the oracle forms
+    the whole forward of the head (about one 262K-token forward of fp64 work)."""
+    run = get_run(key)
+    wl = run.wl
+    L = wl.Lk
+    h = 0
+    q, k, v, do = (run.oracle_head(n) for n in ("q", "k", "v", "do"))
+    dk, dv = (to_f64(run.ohead[n][0], "bf16") for n in ("dk", "dv"))
+    cols = {0, 1, 2, 63, 64, 127, 128, 129, 255, 256, L // 2 - 1, L // 2}
+    pos = stress_positions(wl, "k")
+    if pos is not None:
+        cols.add(int(pos[0, h]))
+    cols = sorted(c for c in cols if 0 <= c < L)
+    t0 = time.perf_counter()
+    # every query row sees key 0: split the rows' sum into ranges formed side by side
+    parts = host_parallel(lambda r: oracle.attn_dkv_cols(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h], cols,
+                                                         wl.causal, rows=r), causal_row_ranges(wl.L, 16))
+    c = parts[0][0]
+    dk_r, dv_r = sum(p[1] for p in parts), sum(p[2] for p in parts)
+    print(f"[{key}] early columns {cols}: oracle {time.perf_counter() - t0:.0f} s", flush=True)
+    check_close(f"dK early cols head {h} {key}", dk[0, c, h], dk_r, "bf16", fro=False)
+    check_close(f"dV early cols head {h} {key}", dv[0, c, h], dv_r, "bf16", fro=False)
 
 
-@pytest.mark.parametrize("key", ["gpt1.2b-L32k-fwd", "gpt7b-L8k",
-                                 pytest.param("gpt7b-L131k", marks=_FULL_ONLY_ON_REQUEST)])
+@pytest.mark.parametrize("key", ["gpt1.2b-L32k-fwd", "gpt7b-L8k", "gpt7b-L131k"])
 def test_full_oracle_every_element(key):
     """A workload as the benchmark would run it, every element of rank 0's
     O and LSE (and dQ, dK, dV) against the full fp64 oracle: seconds for the
     32K forward and the 8K forward and backward (whose launches split every
     walk: two-group forward, dK/dV halves, dQ chunks), about a minute of 16
-    host cores per head for the 131K forward and backward."""
+    host cores per head for the 131K forward and backward (its early key
+    columns, the longest dK/dV sums, included), whose four heads the oracle
+    forms side by side."""
     run = get_run(key)
     wl = run.wl
     assert run.G == 1
@@ -426,20 +455,36 @@ def test_full_oracle_every_element(key):
     do = run.oracle_head("do") if wl.backward else None
     got = {n: to_f64(run.ohead[n][0], "bf16") for n in run.outs}
     lse = run.lse.cpu().numpy()
-    for h in range(wl.Hp):
-        t0 = time.perf_counter()
+
+    # the heads, each cut into row ranges of equal work, side by side; the
+    # ranges' dK, dV terms add up to the whole
+    parts = 16 // wl.Hp if wl.backward else 1
+    tasks = [(h, r) for h in range(wl.Hp) for r in causal_row_ranges(wl.L, parts)]
+
+    def task(hr):
+        h, r = hr
         if wl.backward:
-            dq_r, dk_r, dv_r, o_r, lse_r, _ = oracle.attn_bwd_head(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h],
-                                                                    wl.causal)
-            want_all = (("o", o_r), ("dq", dq_r), ("dk", dk_r), ("dv", dv_r))
+            return oracle.attn_bwd_head(q[0, :, h], k[0, :, h], v[0, :, h], do[0, :, h], wl.causal, rows=r)
+        return oracle.attn_fwd_head(q[0, :, h], k[0, :, h], v[0, :, h], wl.causal)
+
+    t0 = time.perf_counter()
+    res = host_parallel(task, tasks)
+    print(f"[{key}] oracle of {wl.Hp} heads in {len(tasks)} parts: {time.perf_counter() - t0:.0f} s", flush=True)
+    refs = []
+    for h in range(wl.Hp):
+        mine = [x for (hh, _), x in zip(tasks, res) if hh == h]
+        if wl.backward:
+            dq_r, dk_r, dv_r, o_r, lse_r = (sum(x[i] for x in mine) for i in range(5))
+            refs.append(((("o", o_r), ("dq", dq_r), ("dk", dk_r), ("dv", dv_r)), lse_r))
         else:
-            o_r, lse_r = oracle.attn_fwd_head(q[0, :, h], k[0, :, h], v[0, :, h], wl.causal)
-            want_all = (("o", o_r),)
-        print(f"[{key}] head {h}: oracle {time.perf_counter() - t0:.0f} s", flush=True)
+            refs.append(((("o", mine[0][0]),), mine[0][1]))
+    del res
+    for h, (want_all, lse_r) in enumerate(refs):
         for name, want in want_all:
-            st = check_close(f"{name} head {h}", got[name][0, :, h], want, "bf16")
+            st = check_close(f"{name} head {h} {key} (every element)", got[name][0, :, h], want, "bf16")
             print(f"  {name}: max_abs {st['max_abs']:.3e} rel_fro {st['rel_fro']:.3e} "
-                  f"max_err_over_allowed {st['max_err_over_allowed']:.3f}", flush=True)
+                  f"max_err_over_allowed {st['max_err_over_allowed']:.3f} n_over_1e-2 {st['n_over_flat']}",
+                  flush=True)
         err = float(np.max(np.abs(lse[0, h] - lse_r)))
         print(f"  lse: max_abs {err:.3e}", flush=True)
         assert err <= 1e-3

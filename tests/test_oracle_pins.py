@@ -463,6 +463,64 @@ def test_sampled_rows_and_columns(causal):
     np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_column_sums_split_over_row_ranges(causal):
+    # the rows= restriction: a partition of the query rows sums to the whole,
+    # and one row's part is that row's term P_ij (dP_ij - D_i) q_i / sqrt(d)
+    # (dK) and P_ij dO_i (dV), formed here from the full oracle's LSE and D
+    L, d = 150, 16
+    q, k, v, do = (_rand((L, d), s) for s in (42, 43, 44, 45))
+    cols = [0, 5, 63, 64, 149]
+    c, dk_all, dv_all = oracle.attn_dkv_cols(q, k, v, do, cols, causal, row_block=32)
+    parts = [oracle.attn_dkv_cols(q, k, v, do, cols, causal, row_block=32, rows=r)
+             for r in ((0, 7), (7, 64), (64, 65), (65, 150))]
+    np.testing.assert_allclose(sum(p[1] for p in parts), dk_all, atol=1e-12)
+    np.testing.assert_allclose(sum(p[2] for p in parts), dv_all, atol=1e-12)
+    _, _, _, _, lse, D = oracle.attn_bwd_head(q, k, v, do, causal)
+    i = 64
+    _, dk_i, dv_i = parts[2]
+    for n, j in enumerate(c):
+        if causal and j > i:
+            assert not dk_i[n].any() and not dv_i[n].any()
+            continue
+        p_ij = math.exp(q[i] @ k[j] / math.sqrt(d) - lse[i])
+        np.testing.assert_allclose(dk_i[n], p_ij * (do[i] @ v[j] - D[i]) * q[i] / math.sqrt(d), atol=1e-13)
+        np.testing.assert_allclose(dv_i[n], p_ij * do[i], atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_split_over_row_ranges(causal):
+    # attn_bwd_head's rows= restriction: each range fills its own rows of dq,
+    # o, lse and D, and the ranges' dk, dv add up to the whole
+    L, d = 150, 16
+    q, k, v, do = (_rand((L, d), s) for s in (46, 47, 48, 49))
+    whole = oracle.attn_bwd_head(q, k, v, do, causal, row_block=32)
+    ranges = ((0, 40), (40, 41), (41, 150))
+    parts = [oracle.attn_bwd_head(q, k, v, do, causal, row_block=32, rows=r) for r in ranges]
+    for (r0, r1), p in zip(ranges, parts):
+        for i in (0, 3, 4, 5):      # dq, o, lse, D: the range's rows only
+            np.testing.assert_allclose(p[i][r0:r1], whole[i][r0:r1], atol=1e-13)
+            assert not np.any(p[i][:r0]) and not np.any(p[i][r1:])
+    for i in (1, 2):                # dk, dv
+        np.testing.assert_allclose(sum(p[i] for p in parts), whole[i], atol=1e-12)
+
+
+def test_host_parallel_matches_sequential_bit_for_bit():
+    # the GPU tests form oracle parts in host threads, one BLAS thread each
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from gpu_common import causal_row_ranges, host_parallel
+    L, d = 2048, 64
+    heads = [[_rand((L, d), 50 + 4 * h + j) for j in range(4)] for h in range(3)]
+    tasks = [(h, r) for h in range(3) for r in causal_row_ranges(L, 4)]
+    assert [r for h, r in tasks if h == 0][0][0] == 0 and [r for h, r in tasks if h == 0][-1][1] == L
+    res = host_parallel(lambda t: oracle.attn_bwd_head(*heads[t[0]], True, rows=t[1]), tasks)
+    seq = [oracle.attn_bwd_head(*heads[h], True, rows=r) for h, r in tasks]
+    for a, b in zip(res, seq):
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+
+
 @pytest.mark.parametrize("Lq,Lk", [(70, 150), (150, 33)])
 def test_sampled_rows_and_columns_cross_attention(Lq, Lk):
     # the sampled forms with queries and keys of different lengths (bidirectional)
@@ -783,3 +841,35 @@ def test_block_layout_generator_structure():
             assert extra == min(2, i + 1 - len(set(range(max(0, i - 2), i + 1)) | {0}))
     assert not np.array_equal(lay[0], lay[1])                      # random blocks differ per head
     np.testing.assert_array_equal(block_layout(wl), lay)          # seeded
+
+
+# ---------------------------------------------------------------------------
+# the comparison helper every bf16 bar uses: max |x - ref| and the relative
+# Frobenius norm over the whole array, pinned on hand-computed values
+# ---------------------------------------------------------------------------
+
+def test_error_stats_hand_computed():
+    # one element off by -1: max 1, ||diff|| = 1, ||ref|| = sqrt(1 + 4 + 16)
+    st = oracle.error_stats(np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.0, 4.0]))
+    assert st["max_abs"] == 1.0
+    assert st["rel_fro"] == pytest.approx(1.0 / math.sqrt(21.0), rel=1e-15)
+    # the norm runs over every element of a matrix (not a per-row or spectral
+    # norm): diff [[3, 0], [0, -4]] has Frobenius norm 5 (spectral 4), the
+    # reference [[0, 0], [0, 4]] has 4, so the ratio is 1.25 (spectral: 1.0)
+    st = oracle.error_stats(np.array([[3.0, 0.0], [0.0, 0.0]]), np.array([[0.0, 0.0], [0.0, 4.0]]))
+    assert st["max_abs"] == 4.0
+    assert st["rel_fro"] == pytest.approx(1.25, rel=1e-15)
+    # the sign of the difference does not matter; a larger error below the
+    # largest reference entry is still the maximum
+    st = oracle.error_stats(np.array([-5.0, 10.0]), np.array([0.0, 10.5]))
+    assert st["max_abs"] == 5.0
+    assert st["rel_fro"] == pytest.approx(math.sqrt(25.25) / 10.5, rel=1e-15)
+    # an exact match, and a zero reference (then the plain norm of the difference)
+    assert oracle.error_stats(np.arange(6.0), np.arange(6.0)) == {"max_abs": 0.0, "rel_fro": 0.0}
+    st = oracle.error_stats(np.array([0.0, 3.0, -4.0]), np.zeros(3))
+    assert st == {"max_abs": 4.0, "rel_fro": 5.0}
+    # integer-coded bf16 inputs are compared as float64, not in their own type
+    st = oracle.error_stats(np.array([65535], dtype=np.uint16), np.array([0.0]))
+    assert st["max_abs"] == 65535.0
+    # empty arrays have no error
+    assert oracle.error_stats(np.zeros(0), np.zeros(0))["max_abs"] == 0.0

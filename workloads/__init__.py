@@ -140,7 +140,7 @@ WORKLOADS = {
     ]
 }
 
-HEADLINE = "gpt7b-L131k"
+HEADLINE = "L1m"
 
 
 def custom(B, L, H, d, P, dtype="bf16", causal=True, backward=True, index=100,
