@@ -140,10 +140,12 @@ int ulysses_head_to_seq_kv_grad(const void* dx_head, void* dx_seq,
  * m_i + ln(sum_j exp(S_ij - m_i)) over the visible keys of row i, which the
  * backward pass uses to recompute the probabilities.
  * Results are bitwise reproducible for identical calls. The kernels pick
- * their schedule from the launch size (a few hundred query blocks or fewer
- * split each row's key walk in two), so calls that differ in B, heads or L
- * may round a row differently in the last bits; the attention entry points
- * below behave the same way.
+ * their schedule from the launch size: launches of a few hundred query
+ * blocks or fewer split each row's key walk in two or four (forward), and
+ * the backward cuts the walks of small launches into halves or chunks whose
+ * partial sums are added in a fixed order (dQ, dK/dV). Calls that differ in
+ * B, heads or L may therefore round an element differently in the last
+ * bits; the attention entry points below behave the same way.
  */
 int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P,
