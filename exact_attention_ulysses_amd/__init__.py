@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "ULYSSES_OK", 1: "ULYSSES_INVALID_ARGUMENT", 2: "ULYSSES_NOT_
                 6: "ULYSSES_WORKSPACE_TOO_SMALL", 7: "ULYSSES_HIP_ERROR"}
 
 EXPORTS = ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad",
-           "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes",
+           "ulysses_attn_fwd", "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd_noalloc",
            "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa", "ulysses_attn_bwd_gqa_workspace_bytes",
            "ulysses_attn_fwd_block_sparse", "ulysses_attn_bwd_block_sparse",
            "ulysses_attn_bwd_block_sparse_workspace_bytes",
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.ulysses_attn_fwd.restype = ci
     L.ulysses_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64, ci, ci, vp]
     L.ulysses_attn_bwd.restype = ci
+    L.ulysses_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ci, ci, vp]
+    L.ulysses_attn_bwd_noalloc.restype = ci
     L.ulysses_attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, ci, ci]
     L.ulysses_attn_bwd_workspace_bytes.restype = sz
     L.ulysses_attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ci, ci, vp]
@@ -303,9 +305,26 @@ def ulysses_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, workspace, B: int, L: int
     _check(st, "ulysses_attn_bwd")
 
 
+def ulysses_attn_bwd_noalloc(q, k, v, o, d_o, lse, dq, dk, dv, B: int, L: int, H: int, d_h: int, P: int,
+                             causal: bool = True, stream=None) -> None:
+    """ulysses_attn_bwd without a workspace: the library's fixed per-device scratch holds delta and
+    the split walks' partial sums (no device allocation; calls on one device must not overlap)."""
+    torch = _torch()
+    if H % P:
+        raise UlyssesError(2, "ulysses_attn_bwd_noalloc")
+    n = B * L * (H // P) * d_h
+    nl = B * (H // P) * L
+    st = lib().ulysses_attn_bwd_noalloc(
+        _dev(q, "q", n), _dev(k, "k", n, q.dtype), _dev(v, "v", n, q.dtype), _dev(o, "o", n, q.dtype),
+        _dev(d_o, "d_o", n, q.dtype), _dev(lse, "lse", nl, torch.float32),
+        _dev(dq, "dq", n, q.dtype), _dev(dk, "dk", n, q.dtype), _dev(dv, "dv", n, q.dtype),
+        B, L, H, d_h, P, int(bool(causal)), dtype_code(q), _stream(stream))
+    _check(st, "ulysses_attn_bwd_noalloc")
+
+
 __all__ = ["lib", "LIB_PATH", "BF16", "FP32", "UlyssesError", "EXPORTS", "kv_local_heads", "ulysses_seq_to_head",
            "ulysses_head_to_seq", "ulysses_seq_to_head_kv", "ulysses_head_to_seq_kv_grad", "ulysses_attn_fwd",
-           "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa",
+           "ulysses_attn_bwd", "ulysses_attn_bwd_workspace_bytes", "ulysses_attn_bwd_noalloc", "ulysses_attn_fwd_gqa", "ulysses_attn_bwd_gqa",
            "ulysses_attn_bwd_gqa_workspace_bytes", "ulysses_attn_fwd_block_sparse", "ulysses_attn_bwd_block_sparse",
            "ulysses_attn_bwd_block_sparse_workspace_bytes",
            "SPARSE_BLOCK"]

@@ -1023,8 +1023,6 @@ hipError_t launch_delta(const T* o, const T* d_o, float* delta, const AttnShape&
   return hipGetLastError();
 }
 
-inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-
 // Dense bf16 dK/dV launches of few key-block columns C (over batch entries
 // and K/V heads) split every column's walk over the query tiles in two. One
 // workgroup per CU: under the causal mask the longest column is twice the
@@ -1032,10 +1030,21 @@ inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 // and min(1, C / 256) with it (split below 512 columns); bidirectional
 // columns are equally long and pay once the halves still fit the CUs at once
 // (at most 128 columns).
+inline size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+inline size_t delta_bytes(const AttnShape& s) { return round256((size_t)s.B * s.Hq * s.Lq * sizeof(float)); }
+
+// fp32 partial sums of the split dK/dV walks: two [dK | dV][128][d_h] slots per column
+inline size_t dkdv_split_bytes(const AttnShape& s) {
+  const size_t ncol = (size_t)s.B * s.Hk * ((s.Lk + 127) / 128);
+  return round256(2 * ncol * 2 * 128 * (size_t)s.D * sizeof(float));
+}
+
 inline bool dkdv_split(const AttnShape& s) {
   if (!s.bf16 || s.layout) return false;
   const int64_t ncol = (int64_t)s.B * s.Hk * ((s.Lk + 127) / 128);
-  return s.causal ? ncol < 512 : ncol <= 128;
+  if (!(s.causal ? ncol < 512 : ncol <= 128)) return false;
+  return s.ws_cap == 0 || delta_bytes(s) + dkdv_split_bytes(s) <= s.ws_cap;
 }
 
 // Causal splits of at most 128 columns run all their halves at once, so the
@@ -1093,8 +1102,14 @@ inline DqChunks dq_chunks(const AttnShape& s) {
   const double whole = ng2 ? std::max((double)((nkt + 1) / 2), avg) + 2 * rounds(W, 256)
                            : std::max((double)nkt, avg) + 2 * rounds(W, kDqSlots);
   double best_cost = 0.9 * whole;
+  // a capped workspace holds as many dQ slots as remain after delta and the dK/dV split
+  int64_t max_items = kDqMaxItems;
+  if (s.ws_cap) {
+    const size_t used = delta_bytes(s) + (dkdv_split(s) ? dkdv_split_bytes(s) : 0);
+    max_items = used >= s.ws_cap ? 0 : (int64_t)((s.ws_cap - used) / (128 * (size_t)s.D * sizeof(float)));
+  }
   auto consider = [&](int64_t ck, int64_t items, int64_t longest) {
-    if (items > kDqMaxItems) return;
+    if (items > kDqMaxItems || items > max_items) return;
     // one round: every item has a slot of its own
     const double path = items <= kDqSlots ? (double)longest : std::max((double)longest, avg + 0.5 * longest);
     const double cost = path + 2 * rounds(items, kDqSlots) + items / 64.0 + 3;
@@ -1119,7 +1134,7 @@ inline DqChunks dq_chunks(const AttnShape& s) {
 // slots, each 256-byte aligned.
 size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char* base, float** dq_part = nullptr) {
   const size_t ncol = (size_t)s.B * s.Hk * ((s.Lk + kSparseBlock - 1) / kSparseBlock);
-  size_t off = round256((size_t)s.B * s.Hq * s.Lq * sizeof(float));
+  size_t off = delta_bytes(s);
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
     off += round256(bytes);
@@ -1128,7 +1143,7 @@ size_t workspace_layout(const AttnShape& s, bool sparse, SparsePlan* plan, char*
   if (!sparse) {
     if (dkdv_split(s)) {
       SparsePlan pl{};
-      pl.partials = (float*)take(2 * ncol * 2 * 128 * (size_t)s.D * sizeof(float));
+      pl.partials = (float*)take(dkdv_split_bytes(s));
       if (plan) *plan = pl;
     }
     const DqChunks dc = dq_chunks(s);

@@ -34,6 +34,10 @@ struct AttnShape {
   // block-sparse attention (bf16 only): per local query head uint8 layout
   // [Hq][nb][nb] over 128-token blocks, nb = ceil(L / 128); nullptr = dense
   const uint8_t* layout = nullptr;
+  // backward only: upper bound on the workspace (0 = none). A dense bf16
+  // launch then leaves out the split walks whose partial sums would not fit
+  // and takes the whole-walk kernels instead; delta always has to fit.
+  size_t ws_cap = 0;
 };
 
 // bf16 operands, fp32 lse

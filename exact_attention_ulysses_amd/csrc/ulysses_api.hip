@@ -2,6 +2,7 @@
 // dispatch to the kernels. See include/ulysses.h for the contract.
 #include <string.h>
 
+#include <mutex>
 
 #include "../../include/ulysses.h"
 #include "block_sparse.h"
@@ -204,14 +205,17 @@ size_t attn_ws_entry(int64_t B, int64_t Lq, int64_t Lk, int64_t Hq, int64_t Hkv,
   return attn_bwd_workspace_bytes(s, false);
 }
 
-int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+// Validation of a backward call (no HIP call): fills the shape; the
+// workspace is checked against the planner's need unless it is the library's
+// own scratch (workspace == nullptr, capped at ws_cap).
+int attn_bwd_check(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
                    void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Lq,
                    int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal, int dtype,
-                   void* stream, const uint8_t* layout = nullptr, int64_t block = 0) {
-  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv || !workspace) return ULYSSES_INVALID_ARGUMENT;
-  AttnShape s;
+                   const uint8_t* layout, int64_t block, size_t ws_cap, AttnShape* sp) {
+  AttnShape& s = *sp;
   int st = attn_dims(B, Lq, Lk, Hq, Hkv, d_h, P, causal, dtype, &s);
   if (st != ULYSSES_OK) return st;
+  s.ws_cap = ws_cap;
   if (block != 0 || layout) {
     st = sparse_dims(layout, block, Lq, Lk, dtype, &s, true);
     if (st != ULYSSES_OK) return st;
@@ -221,9 +225,10 @@ int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, c
     if (!aligned(p, 16)) return ULYSSES_MISALIGNED;
   if (!aligned(lse, 4)) return ULYSSES_MISALIGNED;
   const size_t need = attn_bwd_workspace_bytes(s, layout != nullptr);
-  if (workspace_bytes < need) return ULYSSES_WORKSPACE_TOO_SMALL;
+  if (workspace ? workspace_bytes < need : need > ws_cap) return ULYSSES_WORKSPACE_TOO_SMALL;
   const int64_t tq = q_bytes(s, dtype), tk = k_bytes(s, dtype);
-  const Range outs[4] = {range_of(dq, tq), range_of(dk, tk), range_of(dv, tk), range_of(workspace, (int64_t)need)};
+  const Range outs[4] = {range_of(dq, tq), range_of(dk, tk), range_of(dv, tk),
+                         range_of(workspace, workspace ? (int64_t)need : 0)};
   const Range ins[7] = {range_of(q, tq), range_of(k, tk), range_of(v, tk), range_of(o, tq), range_of(d_o, tq),
                         range_of(lse, lse_bytes(s)), range_of(layout, layout ? layout_bytes(s) : 0)};
   for (int i = 0; i < 4; ++i) {
@@ -232,11 +237,80 @@ int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, c
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return ULYSSES_ALIASING;
   }
+  return ULYSSES_OK;
+}
+
+int attn_bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                    void* dq, void* dk, void* dv, void* workspace, const AttnShape& s, int dtype, void* stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (dtype == ULYSSES_BF16)
     return report(launch_attn_bwd_bf16(q, k, v, o, d_o, lse, dq, dk, dv, workspace, s, hs));
   return report(launch_attn_bwd_f32((const float*)q, (const float*)k, (const float*)v, (const float*)o,
                                     (const float*)d_o, lse, (float*)dq, (float*)dk, (float*)dv, workspace, s, hs));
+}
+
+int attn_bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int64_t B, int64_t Lq,
+                   int64_t Lk, int64_t Hq, int64_t Hkv, int64_t d_h, int64_t P, int causal, int dtype,
+                   void* stream, const uint8_t* layout = nullptr, int64_t block = 0) {
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv || !workspace) return ULYSSES_INVALID_ARGUMENT;
+  AttnShape s;
+  const int st = attn_bwd_check(q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, Lq, Lk, Hq, Hkv,
+                                d_h, P, causal, dtype, layout, block, 0, &s);
+  if (st != ULYSSES_OK) return st;
+  return attn_bwd_launch(q, k, v, o, d_o, lse, dq, dk, dv, workspace, s, dtype, stream);
+}
+
+// Scratch of the backward entry point that allocates nothing: delta and the
+// partial sums of split walks live here instead of in a caller's workspace.
+// The array's name is a host-side stand-in in host code; kernels get the
+// device address that hipGetSymbolAddress returns for the device at hand.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current.
+int scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return report(e);
+  if (dev < 0 || dev >= kMaxDevices) return ULYSSES_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return report(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return report(e);
+    void* p = nullptr;
+    const hipError_t eg = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return report(e);
+    if (eg != hipSuccess) return report(eg);
+    if (!p) return ULYSSES_HIP_ERROR;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ULYSSES_OK;
+}
+
+// ulysses_attn_bwd with the library's scratch as the workspace: the planner
+// is capped at the scratch size, so only delta has to fit. Every argument is
+// validated before the first HIP call (the device lookup).
+int attn_bwd_noalloc_entry(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                           const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t L, int64_t H,
+                           int64_t d_h, int64_t P, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return ULYSSES_INVALID_ARGUMENT;
+  AttnShape s;
+  int st = attn_bwd_check(q, k, v, o, d_o, lse, dq, dk, dv, nullptr, 0, B, L, L, H, H, d_h, P, causal, dtype,
+                          nullptr, 0, kScratchBytes, &s);
+  if (st != ULYSSES_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (st != ULYSSES_OK) return st;
+  return attn_bwd_launch(q, k, v, o, d_o, lse, dq, dk, dv, ws, s, dtype, stream);
 }
 
 }  // namespace
@@ -331,6 +405,12 @@ int ulysses_attn_bwd_block_sparse(const void* q, const void* k, const void* v, c
   if (!layout) return ULYSSES_INVALID_ARGUMENT;
   return attn_bwd_entry(q, k, v, o, d_o, lse, dq, dk, dv, workspace, workspace_bytes, B, L, L, H_q, H_kv, d_h, P,
                         causal, dtype, stream, layout, block);
+}
+
+int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                             const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t L, int64_t H,
+                             int64_t d_h, int64_t P, int causal, int dtype, void* stream) {
+  return attn_bwd_noalloc_entry(q, k, v, o, d_o, lse, dq, dk, dv, B, L, H, d_h, P, causal, dtype, stream);
 }
 
 const char* ulysses_status_string(int status) {

@@ -183,6 +183,27 @@ size_t ulysses_attn_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t
                                         int64_t P, int causal, int dtype);
 
 /*
+ * ulysses_attn_bwd for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it): the
+ * same arguments without the workspace. Delta and the partial sums of split
+ * walks live in a fixed scratch array of the library, 64 MiB per device,
+ * held from the first call on a device until the process ends. Launches
+ * whose split walks would not fit beside delta take the whole-walk kernels
+ * instead, so results may differ from ulysses_attn_bwd in the last bits
+ * (same tolerance). Delta must fit: B * (H/P) * L <= 16,777,216 rows, else
+ * ULYSSES_WORKSPACE_TOO_SMALL (before any HIP call). The call allocates and
+ * frees nothing. Every call on one device shares that device's scratch:
+ * calls that overlap on one device (two streams, two threads) race and must
+ * be serialised by the caller. Nothing in the scratch needs clearing between
+ * calls; every byte a call reads was written earlier in the same call.
+ */
+int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                             const void* d_o, const float* lse,
+                             void* dq, void* dk, void* dv,
+                             int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P,
+                             int causal, int dtype, void* stream);
+
+/*
  * ulysses_attn_fwd generalised to grouped-query attention and to queries and
  * keys of different lengths (cross-attention). H_q query heads, H_kv K/V heads
  * (global counts; H_q % P == 0, H_q % H_kv == 0, and H_kv % P == 0 or

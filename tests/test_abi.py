@@ -114,6 +114,31 @@ def test_backward_validation():
     assert bwd(ws=A + 5 * GB) == 5                   # workspace overlaps lse
 
 
+def bwd_noalloc(B=1, L=1024, H=8, d=128, P=4, causal=1, dtype=U.BF16, **ptrs):
+    names = ["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"]
+    p = {n: A + i * GB for i, n in enumerate(names)}
+    p.update(ptrs)
+    return U.lib().ulysses_attn_bwd_noalloc(*[p[n] for n in names], B, L, H, d, P, causal, dtype, None)
+
+
+def test_backward_noalloc_validation():
+    # every rejection happens before the first HIP call (the device lookup)
+    for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert bwd_noalloc(**{n: None}) == 1, n
+    assert bwd_noalloc(B=0) == 1
+    assert bwd_noalloc(causal=3) == 1
+    assert bwd_noalloc(H=8, P=3) == 2
+    assert bwd_noalloc(d=96) == 3
+    assert bwd_noalloc(dtype=5) == 3
+    assert bwd_noalloc(dk=A + 7 * GB + 2) == 4
+    assert bwd_noalloc(lse=A + 5 * GB + 2) == 4
+    assert bwd_noalloc(dq=A + 64) == 5                   # dq overlaps q
+    assert bwd_noalloc(dv=A + 7 * GB + 256) == 5         # dv overlaps dk
+    # delta [B][H/P][L] fp32 must fit the 64 MiB scratch: 3 x 2 x 2^22 rows do not
+    big = {n: A + i * 8 * GB for i, n in enumerate(["q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"])}
+    assert bwd_noalloc(B=3, L=1 << 22, H=4, P=2, **big) == 6
+
+
 def test_workspace_size():
     lib = U.lib()
     # delta [B][H/P][L] fp32, rounded up to 256 bytes
