@@ -421,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       // rows past the end, and rows that see no key (LSE -inf, block layouts
       // only), get lse = +inf, so their probabilities are exactly 0
       lse2s[buf][tid] = (!row_ok || lse_r == -INFINITY) ? INFINITY : lse_r * kLog2e;
-      dls[buf][tid] = row_ok ? dl_r : 0.f;
+      dls[buf][tid] = row_ok ? -dl_r : 0.f;   // -delta: the dP accumulator starts from it
     }
   };
 
@@ -454,7 +454,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         sc[u] = f32x16{};
-        dp[u] = f32x16{};
+        // dP - delta: the accumulator starts from -delta of its rows (element
+        // 4a + i holds row 32u + 8a + 4 * (lane / 32) + i), so the MFMAs leave
+        // dP - delta and the softmax step needs no subtraction
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 nd4 = *reinterpret_cast<const f32x4*>(&dls[cur][32 * u + 8 * a + 4 * hl]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[u][4 * a + i] = nd4[i];
+        }
         // all of the half's Q and dO fragments are read before its MFMAs
         // start, so that the MFMAs do not each wait on a fresh LDS read
         bf16x8 qa[KS], da[KS];
@@ -476,12 +484,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
         for (int a = 0; a < 4; ++a) {
           const int r0 = 32 * u + 8 * a + 4 * hl;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[cur][r0]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dls[cur][r0]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * a + i;
             float p = __builtin_amdgcn_exp2f(fmaf(sc[u][e], sl2, -l4[i]));
-            float ds = p * (dp[u][e] - d4[i]);
+            float ds = p * dp[u][e];
             if (MASK && key > q0 + r0 + i) {  // keys above the query row
               p = 0.f;
               ds = 0.f;
