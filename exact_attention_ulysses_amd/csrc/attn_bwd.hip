@@ -55,6 +55,7 @@ namespace ulysses {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kDqXcdRun = 64;   // one-walk dQ workgroups an XCD holds at once (two per CU)
 
 // S(m) = sum over x = 1..m of ceil(x / t): the number of chunks of query
 // blocks 0..m-1 when block x - 1 (2x key tiles of 64 under the causal mask)
@@ -316,9 +317,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     // neighbouring key blocks, which read the same query tiles a few steps
     // apart. Runs go to XCDs 0..7 and 7..0 in alternate rounds of 256 jobs,
     // which keeps the causal work of the XCDs even.
-    const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
-    const int round = j >> 5;
-    col = 256 * round + 32 * ((round & 1) ? 7 - x : x) + (j & 31);
+    col = xcd_run_job((int)blockIdx.x, 32);
     if (col >= nkb_all * nhb) return;   // grid rounded up to whole rounds
   }
   const int kb = SPARSE ? col % (nb) : col / nhb;
@@ -603,8 +602,17 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;   // row group of this wave
   const int grp = NG == 2 ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;   // key half (NG = 2)
-  int qb = nqb - 1 - (int)blockIdx.x / nhb;
-  int hb = blockIdx.x % nhb;               // (batch, query head) pair
+  // jobs (query block, head pair), longest rows first; the dense one-walk
+  // launch takes them in runs of 64 per XCD (two workgroups per CU), so that
+  // the blocks on one XCD walk the same key tiles a few steps apart and
+  // share them through its L2
+  int job = (int)blockIdx.x;
+  if constexpr (!SPARSE && NG == 1 && !CHUNK) {
+    job = xcd_run_job(job, kDqXcdRun);
+    if (job >= nqb * nhb) return;          // grid rounded up to whole rounds
+  }
+  int qb = nqb - 1 - job / nhb;
+  int hb = job % nhb;                      // (batch, query head) pair
   int chunk = 0, nchunk = 1;               // this workgroup's part of the block's key walk (CHUNK)
   if constexpr (CHUNK) {
     const int i = blockIdx.x;
@@ -1211,7 +1219,7 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
     hipLaunchKernelGGL((bwd_sparse_reduce_kernel<D, true>), dim3(1024), dim3(256), 0, stream, plan, nkhb, s.Lk,
                        s.Hk, (__bf16*)dk, (__bf16*)dv, scale, ncol, nkb, ck);
   } else {
-    const unsigned grid = (unsigned)((nkb * nkhb + 255) / 256 * 256);   // whole rounds of 256 jobs
+    const unsigned grid = xcd_run_grid((long long)nkb * nkhb, 32);   // whole rounds of 256 jobs
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, CAUSAL, false>), dim3(grid), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dk, (__bf16*)dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale, nullptr, 0,
@@ -1242,7 +1250,8 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, 0, nullptr);
   else
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false>), dim3(xcd_run_grid((long long)nqb * nhb, kDqXcdRun)),
+                       dim3(256), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, 0, nullptr);
   return hipGetLastError();

@@ -50,6 +50,7 @@ namespace ulysses {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kFwdXcdRun = 32;   // dense forward workgroups an XCD holds at once (one per CU)
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Block layouts: workgroup = 4 waves x 32 query rows, one 128-row query block;
@@ -489,7 +490,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool groupA = wave < 4;
   const int gtid = tid & 255;                // thread index within the group
-  const int bid = blockIdx.x;
+  // jobs (query block, head pair), longest rows first, in runs of 32 per XCD
+  // (one workgroup per CU): the blocks on one XCD walk the same key tiles a
+  // few steps apart and share them through its L2
+  const int bid = xcd_run_job((int)blockIdx.x, kFwdXcdRun);
+  if (bid >= nqb * nhb) return;              // grid rounded up to whole rounds
   const int qb = nqb - 1 - bid / nhb;        // longest rows first
   const int hb = bid % nhb;
   const int b = hb / Hq, h = hb - b * Hq;
@@ -752,7 +757,8 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
                          (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
                          s.Hk, s.Hq / s.Hk, nqb, nhb, sl2);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb2 * nhb), dim3(512), 0, stream,
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3(xcd_run_grid((long long)nqb2 * nhb, kFwdXcdRun)),
+                         dim3(512), 0, stream,
                          (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
                          s.Hk, s.Hq / s.Hk, nqb2, nhb, sl2);
   }

@@ -44,6 +44,26 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 }
 
 // ---------------------------------------------------------------------------
+// XCD-aware job order. The eight XCDs of the chip each have their own L2, and
+// workgroup i of a launch runs on XCD i mod 8. Attention workgroups that walk
+// the same tiles at the same time share them through the L2 only when they
+// sit on one XCD, so this map gives each XCD runs of `run` consecutive jobs
+// (run = the workgroups an XCD holds at once), the XCDs taking the runs of a
+// round of 8 * run jobs in alternating directions to keep their work even
+// when jobs shrink (longest first). Launches round their grid up to whole
+// rounds; workgroups past the last job exit at once.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int xcd_run_job(int bid, int run) {
+  const int x = bid & 7, j = bid >> 3;
+  const int round = j / run;
+  return 8 * run * round + run * ((round & 1) ? 7 - x : x) + (j - round * run);
+}
+
+__host__ __device__ inline unsigned xcd_run_grid(long long jobs, int run) {
+  return (unsigned)((jobs + 8LL * run - 1) / (8LL * run) * (8LL * run));
+}
+
+// ---------------------------------------------------------------------------
 // launch-side error reporting (thread-local last error text)
 // ---------------------------------------------------------------------------
 void set_last_hip_error(hipError_t e);
