@@ -311,14 +311,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       slot = 2 * col;
     }
   } else if constexpr (!SPARSE) {
-    // jobs (key block kb, head pair hb) in order kb * nhb + hb, longest first.
-    // Workgroup i runs on XCD i mod 8 (round-robin dispatch); each XCD takes
-    // runs of 32 consecutive jobs, so that the workgroups sharing its L2 walk
-    // neighbouring key blocks, which read the same query tiles a few steps
-    // apart. Runs go to XCDs 0..7 and 7..0 in alternate rounds of 256 jobs,
-    // which keeps the causal work of the XCDs even.
-    col = xcd_run_job((int)blockIdx.x, 32);
-    if (col >= nkb_all * nhb) return;   // grid rounded up to whole rounds
+    // jobs (key block kb, head pair hb), longest first. Workgroup i runs on
+    // XCD i mod 8 (round-robin dispatch); each XCD takes runs of 32 jobs,
+    // neighbouring key blocks of one head pair where the head pairs divide a
+    // round, so that the workgroups sharing its L2 read the same query tiles
+    // a few steps apart. Runs go to XCDs 0..7 and 7..0 in alternate rounds of
+    // 256 jobs, which keeps the causal work of the XCDs even.
+    int rank, hbr;
+    if (!xcd_run_block((int)blockIdx.x, 32, nhb, nkb_all, &rank, &hbr)) return;   // grid rounded up
+    col = rank * nhb + hbr;
   }
   const int kb = SPARSE ? col % (nb) : col / nhb;
   const int hb = SPARSE ? col / (nb) : col % nhb;   // (batch, key head) pair
@@ -606,13 +607,12 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
   // launch takes them in runs of 64 per XCD (two workgroups per CU), so that
   // the blocks on one XCD walk the same key tiles a few steps apart and
   // share them through its L2
-  int job = (int)blockIdx.x;
+  int rank = (int)blockIdx.x / nhb;
+  int hb = (int)blockIdx.x % nhb;          // (batch, query head) pair
   if constexpr (!SPARSE && NG == 1 && !CHUNK) {
-    job = xcd_run_job(job, kDqXcdRun);
-    if (job >= nqb * nhb) return;          // grid rounded up to whole rounds
+    if (!xcd_run_block((int)blockIdx.x, kDqXcdRun, nhb, nqb, &rank, &hb)) return;   // grid rounded up
   }
-  int qb = nqb - 1 - job / nhb;
-  int hb = job % nhb;                      // (batch, query head) pair
+  int qb = nqb - 1 - rank;
   int chunk = 0, nchunk = 1;               // this workgroup's part of the block's key walk (CHUNK)
   if constexpr (CHUNK) {
     const int i = blockIdx.x;

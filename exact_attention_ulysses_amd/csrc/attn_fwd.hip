@@ -493,10 +493,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   // jobs (query block, head pair), longest rows first, in runs of 32 per XCD
   // (one workgroup per CU): the blocks on one XCD walk the same key tiles a
   // few steps apart and share them through its L2
-  const int bid = xcd_run_job((int)blockIdx.x, kFwdXcdRun);
-  if (bid >= nqb * nhb) return;              // grid rounded up to whole rounds
-  const int qb = nqb - 1 - bid / nhb;        // longest rows first
-  const int hb = bid % nhb;
+  int rank, hb;
+  if (!xcd_run_block((int)blockIdx.x, kFwdXcdRun, nhb, nqb, &rank, &hb)) return;   // grid rounded up
+  const int qb = nqb - 1 - rank;             // longest rows first
   const int b = hb / Hq, h = hb - b * Hq;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
   const size_t qoff = ((size_t)b * Lq * Hq + h) * D;

@@ -63,6 +63,27 @@ __host__ __device__ inline unsigned xcd_run_grid(long long jobs, int run) {
   return (unsigned)((jobs + 8LL * run - 1) / (8LL * run) * (8LL * run));
 }
 
+// Jobs (block rank, head pair hb), the ranks longest first: job j is rank
+// j / nhb of head pair j % nhb. With xcd_run_job's runs, a round of
+// 8 * run consecutive jobs holds (8 * run) / nhb ranks of every head pair;
+// when nhb divides the round they are taken head by head, so that a run is
+// consecutive ranks of one head pair (each XCD then streams the tiles of
+// one head) rather than every head's at once. Returns false past the last
+// job.
+__device__ __forceinline__ bool xcd_run_block(int bid, int run, int nhb, int nranks, int* rank, int* hb) {
+  const int j = xcd_run_job(bid, run);
+  const int span = 8 * run;
+  if (span % nhb == 0) {
+    const int round = j / span, i = j - round * span, per = span / nhb;
+    *hb = i / per;
+    *rank = round * per + (i - *hb * per);
+  } else {
+    *rank = j / nhb;
+    *hb = j - *rank * nhb;
+  }
+  return *rank < nranks;
+}
+
 // ---------------------------------------------------------------------------
 // launch-side error reporting (thread-local last error text)
 // ---------------------------------------------------------------------------
