@@ -11,13 +11,16 @@
 // (token, head-group) slab of H/P * d_h elements: 128 B .. 1 KiB for the
 // supported d_h and dtypes, always a whole number of 128-byte lines. The
 // kernel therefore copies 16-byte words straight from HBM to HBM: a wave's
-// 64 lanes move 1 KiB of consecutive seq-layout words, which on the
-// head-layout side form runs of at least 128 contiguous bytes, so every line
-// read and written is a full line. Staging through LDS would add a round
-// trip without making any access wider. Values are never converted; bits are
-// copied as they are. Both
-// directions walk the seq-layout tensor in order (seq_to_head reads it,
-// head_to_seq writes it), so the runs are always on the head-layout side.
+// 64 lanes move 1 KiB of consecutive words of the tensor it walks, which on
+// the other side form runs of at least 128 contiguous bytes, so every line
+// read and written is a full line. Staging through LDS adds a round trip
+// without making any access wider (measured: LDS-staged tiles were no
+// faster). Values are never converted; bits are copied as they are. The
+// kernel walks the seq-layout tensor in order (seq_to_head reads it,
+// head_to_seq writes it) except for seq_to_head with runs of 256 bytes or
+// less, which walks the head layout (gathering its runs and writing in
+// order): with 32 destination groups of 256-byte runs that measured 2 %
+// faster than scattering them.
 //
 // K/V heads of grouped-query attention (pinyu.ai, section "Head-count
 // constraints"): with fewer K/V heads than ranks, every rank receives the one
@@ -147,7 +150,7 @@ hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, 
   a.fU = make_fastdiv(U);
   a.rep = 1;
   a.srep = 0;
-  // Both directions walk the seq-layout tensor [r][b][t][g][w] (g: head group,
+  // By default both directions walk the seq-layout tensor [r][b][t][g][w] (g: head group,
   // P / rep of them) and find the word in the head-layout tensor
   // [g*rep + j][b][r][t][w]: seq_to_head scatters (rep copies), head_to_seq
   // gathers. Either way the seq-layout side is read or written in order and
@@ -162,9 +165,23 @@ hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, 
   a.s3 = s.rep * rank_words; // g
   a.rep = s.rep;
   a.srep = rank_words;
+  // seq_to_head with short runs walks the head layout [g][b][r][t][w] in
+  // order instead, gathering from the seq layout (strides below)
+  const bool head_walk = seq_to_head && s.rep == 1 && U <= 16;
+  if (head_walk) {
+    const uint32_t G = P;
+    a.f1 = make_fastdiv(B);    // extents [g][b][r][t][w]
+    a.f2 = make_fastdiv(P);
+    a.f3 = make_fastdiv(Lp);
+    a.s0 = U;                  // g
+    a.s1 = Lp * G * U;         // b
+    a.s2 = B * Lp * G * U;     // r
+    a.s3 = G * U;              // t
+  }
   const uint32_t per_block = kThreads * kUnroll;
   const uint32_t blocks = (a.total + per_block - 1) / per_block;
-  if (seq_to_head)
+  // the walked tensor is the source (scatter) or the destination (gather)
+  if (seq_to_head != head_walk)
     hipLaunchKernelGGL(perm_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(perm_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
