@@ -14,6 +14,13 @@ the whole step time (transposes included); per-op figures come from HIP
 events recorded on the launch stream around every call in the timed steps.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Warm-up: W untimed steps when --warmup is given; by default as many steps as
+fill --warmup-seconds (1 s, at least 3 steps), so that short steps are timed
+at the clocks the GPU holds under sustained load rather than while it ramps
+up from idle (measured on the 32K forward-only workload: 0.67 ms per forward
+after 3 warm-up steps, 0.58 ms after 600). The line's "warmup" is the count
+run.
     python bench.py --gemm-ceiling      # vendor bf16 GEMM rate, for context
 
 HBM traffic of the dominant op (roofline "traffic"): two rocprofv3 counter
@@ -137,7 +144,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as fill --warmup-seconds, at least 3)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536,
@@ -359,8 +368,22 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        warmup_steps = args.warmup
+    else:
+        # whole steps until --warmup-seconds of them have run (at least 3),
+        # the host waiting for the GPU every 4 steps to read the clock
+        warmup_steps = 0
+        w0 = time.perf_counter()
+        while True:
+            step()
+            warmup_steps += 1
+            if warmup_steps % 4 == 3:
+                torch.cuda.synchronize()
+                if time.perf_counter() - w0 >= args.warmup_seconds or warmup_steps >= 100000:
+                    break
     torch.cuda.synchronize()
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
            for _ in range(args.steps)]
@@ -470,7 +493,7 @@ def main():
         + (" grouped-query" if Hk != H else "") + (" cross-" if Lk != L else " ") + "attn")
     line = {
         "metric": metric, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "warmup": warmup_steps, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded, device-generated)",
         "config": {"workload": wl.key, "B": B, "L": L, "H": H, "d_h": d, "P": P, "local_heads": Hh,
                    "causal": causal, "backward": wl.backward, "parallelism": "1 GPU, P virtual ranks",

@@ -57,13 +57,8 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kDqXcdRun = 64;   // one-walk dQ workgroups an XCD holds at once (two per CU)
 
-// S(m) = sum over x = 1..m of ceil(x / t): the number of chunks of query
-// blocks 0..m-1 when block x - 1 (2x key tiles of 64 under the causal mask)
-// is cut into ceil(x / t) parts of at most 2t tiles.
-__host__ __device__ inline int chunk_prefix(int m, int t) {
-  const int a = m / t, r = m - a * t;
-  return t * a * (a + 1) / 2 + r * (a + 1);
-}
+// Chunked causal walks (common.h): 128-row block x - 1 has 2x key tiles of
+// 64 under the causal mask, cut into ceil(x / t) parts of at most 2t tiles.
 
 // delta[b][h][i] = sum_e dO[b][i][h][e] * O[b][i][h][e]; D/8 lanes per row.
 template <typename T, int D>
@@ -285,24 +280,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
   }
   if constexpr (SPLIT) {
     if (CAUSAL && ck > 0) {
-      // key block kb = nkb_all - x cut into ceil(x / ck) parts, columns
-      // longest first; the items before key block kb number
-      // nhb (S(nkb_all) - S(x)) with S(m) = chunk_prefix(m, ck)
+      // key block kb = nkb_all - x (its column has x query blocks) cut into
+      // ceil(x / ck) parts, columns longest first
       const int i = blockIdx.x;
-      const int sn = chunk_prefix(nkb_all, ck);
-      int lo = 1, hi = nkb_all;   // the smallest x whose predecessors number at most i
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (nhb * (sn - chunk_prefix(mid, ck)) <= i)
-          hi = mid;
-        else
-          lo = mid + 1;
-      }
-      nchunk = (lo + ck - 1) / ck;
-      const int loc = i - nhb * (sn - chunk_prefix(lo, ck));
-      const int hbi = loc / nchunk;
-      chunk = loc - hbi * nchunk;
-      col = (nkb_all - lo) * nhb + hbi;
+      int x, hbi;
+      causal_chunk_item(i, nkb_all, nhb, ck, &x, &hbi, &chunk, &nchunk);
+      col = (nkb_all - x) * nhb + hbi;
       slot = i - chunk;
     } else {
       col = (int)blockIdx.x >> 1;
@@ -617,24 +600,10 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
   if constexpr (CHUNK) {
     const int i = blockIdx.x;
     if constexpr (CAUSAL) {
-      // block qb = x - 1 has ceil(x / ck) chunks; blocks run longest first,
-      // so the work items before block x number nhb (S(nqb) - S(x)) with
-      // S(m) = chunk_prefix(m, ck); the block holding item i is the smallest
-      // x whose predecessors number at most i
-      const int sn = chunk_prefix(nqb, ck);
-      int lo = 1, hi = nqb;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (nhb * (sn - chunk_prefix(mid, ck)) <= i)
-          hi = mid;
-        else
-          lo = mid + 1;
-      }
-      nchunk = (lo + ck - 1) / ck;
-      const int loc = i - nhb * (sn - chunk_prefix(lo, ck));
-      qb = lo - 1;
-      hb = loc / nchunk;
-      chunk = loc - hb * nchunk;
+      // block qb = x - 1 has ceil(x / ck) chunks, blocks longest first
+      int x;
+      causal_chunk_item(i, nqb, nhb, ck, &x, &hb, &chunk, &nchunk);
+      qb = x - 1;
     } else {
       nchunk = ck;   // every block: ck chunks
       const int bi = i / nchunk;

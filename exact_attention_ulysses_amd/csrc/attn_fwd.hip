@@ -282,9 +282,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / WPG, wq = wave % WPG;
   const int gtid = tid % GT;                 // thread index within the group
-  const int bid = blockIdx.x;
-  const int qb = nqb - 1 - bid / nhb;        // longest rows first
-  const int hb = bid % nhb;
+  // jobs (query block, head pair), longest rows first, in runs of 32 per
+  // XCD as in the ping-pong kernel
+  int rank, hb;
+  if (!xcd_run_block((int)blockIdx.x, kFwdXcdRun, nhb, nqb, &rank, &hb)) return;   // grid rounded up
+  const int qb = nqb - 1 - rank;
   const int b = hb / Hq, h = hb - b * Hq;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
   const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
@@ -748,11 +750,13 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
     const int64_t W = (int64_t)nqb2 * nhb;
     if (CAUSAL ? W < kSplit4CausalBelow : W <= kSplit4FullUpTo) {
       const int nqb64 = (s.Lq + 63) / 64;
-      hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL, 4>), dim3((unsigned)nqb64 * nhb), dim3(512), 0, stream,
+      hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL, 4>), dim3(xcd_run_grid((long long)nqb64 * nhb, kFwdXcdRun)),
+                         dim3(512), 0, stream,
                          (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
                          s.Hk, s.Hq / s.Hk, nqb64, nhb, sl2);
     } else if (CAUSAL ? W < kSplitCausalBelow : W <= kSplitFullUpTo)
-      hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(512), 0, stream,
+      hipLaunchKernelGGL((attn_fwd_split_bf16_kernel<D, CAUSAL>), dim3(xcd_run_grid((long long)nqb * nhb, kFwdXcdRun)),
+                         dim3(512), 0, stream,
                          (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, s.Lq, s.Lk, s.Hq,
                          s.Hk, s.Hq / s.Hk, nqb, nhb, sl2);
     else

@@ -85,6 +85,41 @@ __device__ __forceinline__ bool xcd_run_block(int bid, int run, int nhb, int nra
 }
 
 // ---------------------------------------------------------------------------
+// Chunked causal walks. Under the causal mask query block x - 1 (x = 1 ..
+// nblk) walks a number of key tiles proportional to x; cutting it into
+// ceil(x / t) near-equal parts bounds every part by the length of t blocks'
+// worth of diagonal. Work items are numbered blocks longest first, head pairs
+// inner, a block's parts consecutive.
+// S(m) = sum over x = 1..m of ceil(x / t): the parts of blocks 0..m-1.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int chunk_prefix(int m, int t) {
+  const int a = m / t, r = m - a * t;
+  return t * a * (a + 1) / 2 + r * (a + 1);
+}
+
+// Work item i of nhb * S(nblk): block x - 1 (returned as x), head pair hb,
+// part `chunk` of nchunk = ceil(x / t). The items before block x number
+// nhb (S(nblk) - S(x)); x is the smallest block whose predecessors number at
+// most i.
+__device__ inline void causal_chunk_item(int i, int nblk, int nhb, int t, int* x, int* hb, int* chunk,
+                                         int* nchunk) {
+  const int sn = chunk_prefix(nblk, t);
+  int lo = 1, hi = nblk;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (nhb * (sn - chunk_prefix(mid, t)) <= i)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  *x = lo;
+  *nchunk = (lo + t - 1) / t;
+  const int loc = i - nhb * (sn - chunk_prefix(lo, t));
+  *hb = loc / *nchunk;
+  *chunk = loc - *hb * *nchunk;
+}
+
+// ---------------------------------------------------------------------------
 // launch-side error reporting (thread-local last error text)
 // ---------------------------------------------------------------------------
 void set_last_hip_error(hipError_t e);
