@@ -65,3 +65,12 @@ def fwd_groups(B, Lq, Hq, causal):
     if W < 384 if causal else W <= 128:
         return 2
     return 1
+
+
+def dkdv_whole_walks(B, L, Hk, causal):
+    """True when a dense bf16 dK/dV launch gives every key-block column one
+    workgroup walking all its query tiles: causal launches of at least 512
+    columns (batch x local K/V heads x 128-token key blocks), bidirectional
+    ones of more than 128 (below those the walks are split)."""
+    ncol = B * Hk * -(-L // 128)
+    return ncol >= 512 if causal else ncol > 128
