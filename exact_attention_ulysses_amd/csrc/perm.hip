@@ -41,6 +41,12 @@ namespace {
 // 83 % of HBM peak against 70-78 % for 256 threads x 1-4 words).
 constexpr int kThreads = 64;
 constexpr int kUnroll = 1;
+// seq_to_head walking the head layout (runs of 256 bytes or less) in
+// workgroups of 4 waves instead: at 1M tokens (32 head groups of 256-byte
+// runs) 6.31-6.34 TB/s against 6.04-6.10 with one wave, while 128, 192,
+// 320, 384, 512 and 1024 threads all measured 5.4-6.0 TB/s, and the other
+// forms lose with larger workgroups.
+constexpr int kWalkThreads = 256;
 
 // The kernel walks one tensor's words in order ("own" index) and computes
 // where each word sits in the other tensor:
@@ -55,14 +61,14 @@ struct PermArgs {
   uint32_t rep, srep;        // copies of each word and the distance between them (scatter)
 };
 
-template <bool GATHER>
-__global__ __launch_bounds__(kThreads) void perm_kernel(PermArgs a) {
-  const uint32_t base = blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+template <bool GATHER, int THREADS>
+__global__ __launch_bounds__(THREADS) void perm_kernel(PermArgs a) {
+  const uint32_t base = blockIdx.x * (THREADS * kUnroll) + threadIdx.x;
   u32x4 val[kUnroll];
   uint32_t dsto[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t idx = base + u * kThreads;
+    const uint32_t idx = base + u * THREADS;
     if (!GATHER && idx < a.total) val[u] = __builtin_nontemporal_load(a.src + idx);
     const uint32_t run = fdiv(idx, a.fU);
     const uint32_t w = idx - run * a.fU.d;
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void perm_kernel(PermArgs a) {
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t idx = base + u * kThreads;
+    const uint32_t idx = base + u * THREADS;
     if (idx < a.total) {
       if (GATHER)
         __builtin_nontemporal_store(val[u], a.dst + idx);
@@ -178,13 +184,17 @@ hipError_t launch_seq_head_perm(const void* src, void* dst, const PermShape& s, 
     a.s2 = B * Lp * G * U;     // r
     a.s3 = G * U;              // t
   }
-  const uint32_t per_block = kThreads * kUnroll;
-  const uint32_t blocks = (a.total + per_block - 1) / per_block;
   // the walked tensor is the source (scatter) or the destination (gather)
-  if (seq_to_head != head_walk)
-    hipLaunchKernelGGL(perm_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, a);
+  if (head_walk) {
+    const uint32_t blocks = (a.total + kWalkThreads * kUnroll - 1) / (kWalkThreads * kUnroll);
+    hipLaunchKernelGGL((perm_kernel<true, kWalkThreads>), dim3(blocks), dim3(kWalkThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  const uint32_t blocks = (a.total + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  if (seq_to_head)
+    hipLaunchKernelGGL((perm_kernel<false, kThreads>), dim3(blocks), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(perm_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((perm_kernel<true, kThreads>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
