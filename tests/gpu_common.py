@@ -113,7 +113,7 @@ def shared_head_allowed(parts, want, dtype):
 
 
 def host_cores() -> int:
-    """Host threads this process may use (the machine's CPU share when OMP_NUM_THREADS states it)."""
+    """Host threads this process may use (the host's CPU share when OMP_NUM_THREADS states it)."""
     n = len(os.sched_getaffinity(0))
     try:
         n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
