@@ -6,8 +6,12 @@ dim 64 or 128, causal or bidirectional (cross-attention when the lengths
 differ), bf16 or fp32. Most of them are small launches, which the kernels
 run with split key and query walks; the wide cases (many heads over few
 tokens) reach the single-walk schedules at sizes the oracle still finishes
-in a moment. Twelve more cases run block layouts (a window, global and
-random blocks per row, some block rows emptied; bf16, self-attention).
+in a moment. 120 cases in all; 36 more run block layouts (a window, global
+and random blocks per row, some block rows emptied; bf16, self-attention).
+The gradient of a K/V head shared by several query heads is held to the
+sum of its parts' bars in both element types (gpu_common.shared_head_allowed):
+in fp32, four query heads over ~350-630 tokens give dV elements 1.03-1.28e-5
+off (sums of up to ~2,500 products in fp32), inside four parts' 1e-5.
 Forward and backward go through the generalised entry points
 and are held to the same bars as every other parity test, with the bf16
 elementwise bar widened by the bound on rounding P and dS to bf16 inside the
@@ -48,7 +52,7 @@ def _draw_case(i):
     return B, Lq, Lk, Hq, Hkv, d, P, causal, dtype
 
 
-CASES = [_draw_case(i) for i in range(36)]
+CASES = [_draw_case(i) for i in range(120)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -118,9 +122,8 @@ def test_sweep_parity(case):
             parts["dK"][h % G, b, :, h // G] = r[1]
             parts["dV"][h % G, b, :, h // G] = r[2]
     for name, got, want in (("dK", dk, dk_r), ("dV", dv, dv_r)):
-        allowed = shared_head_allowed(parts[name], want, dtype) if dtype == "bf16" else None
-        check_close(f"{name} {tag}", to_f64(got, dtype), want, dtype, allowed=allowed,
-                    abs_sum=asum[name.lower()])
+        check_close(f"{name} {tag}", to_f64(got, dtype), want, dtype,
+                    allowed=shared_head_allowed(parts[name], want, dtype), abs_sum=asum[name.lower()])
 
 
 def _draw_sparse_case(i):
@@ -136,7 +139,7 @@ def _draw_sparse_case(i):
     return B, L, Hkl * G * P, Hkl * P, d, P, causal, lay   # lay: window, global, random, empty rows
 
 
-SPARSE_CASES = [_draw_sparse_case(i) for i in range(12)]
+SPARSE_CASES = [_draw_sparse_case(i) for i in range(36)]
 
 
 @pytest.mark.parametrize("case", range(len(SPARSE_CASES)))
