@@ -2,6 +2,7 @@
 // dispatch to the kernels. See include/ulysses.h for the contract.
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/ulysses.h"
@@ -35,16 +36,26 @@ inline bool valid_dtype(int dtype) { return dtype == ULYSSES_BF16 || dtype == UL
 
 inline bool valid_head_dim(int64_t d) { return d == 64 || d == 128; }
 
+// The product of positive factors is at most cap (checked factor by factor,
+// so that no partial product can overflow).
+inline bool product_at_most(std::initializer_list<int64_t> factors, int64_t cap) {
+  int64_t p = 1;
+  for (const int64_t f : factors) {
+    if (p > cap / f) return false;
+    p *= f;
+  }
+  return true;
+}
+
 // common size checks; returns OK or the status to report
 int check_dims(int64_t B, int64_t L, int64_t H, int64_t d_h, int64_t P, int dtype) {
   if (B <= 0 || L <= 0 || H <= 0 || d_h <= 0 || P <= 0) return ULYSSES_INVALID_ARGUMENT;
   if (!valid_dtype(dtype)) return ULYSSES_UNSUPPORTED;
   if (H % P != 0) return ULYSSES_NOT_DIVISIBLE;
   if (!valid_head_dim(d_h)) return ULYSSES_UNSUPPORTED;
-  // every product below stays far from int64 overflow once each factor is capped
   if (B > (int64_t(1) << 30) || L > (int64_t(1) << 30) || H > (int64_t(1) << 20)) return ULYSSES_UNSUPPORTED;
-  const int64_t words = B * L * H * d_h * elem_size(dtype) / 16;
-  if (words >= kMaxWords) return ULYSSES_UNSUPPORTED;
+  // each tensor below 32 GiB (kMaxWords 16-byte words)
+  if (!product_at_most({B, L, H, d_h, elem_size(dtype)}, kMaxWords * 16 - 1)) return ULYSSES_UNSUPPORTED;
   return ULYSSES_OK;
 }
 
@@ -93,9 +104,10 @@ int kv_perm_entry(const void* src, void* dst, int64_t B, int64_t L, int64_t Hkv,
   if (B > (int64_t(1) << 30) || L > (int64_t(1) << 30) || Hkv > (int64_t(1) << 20) || P > (int64_t(1) << 20))
     return ULYSSES_UNSUPPORTED;
   const int64_t es = elem_size(dtype);
+  // the head-side tensor (rep times the seq side) below 32 GiB
+  if (!product_at_most({P, B, L, Hl, d_h, es}, kMaxWords * 16 - 1)) return ULYSSES_UNSUPPORTED;
   const int64_t seq_bytes = B * L * Hkv * d_h * es;
   const int64_t head_bytes = P * B * L * Hl * d_h * es;   // = seq_bytes * rep
-  if (head_bytes / 16 >= kMaxWords) return ULYSSES_UNSUPPORTED;
   if (!aligned(src, 16) || !aligned(dst, 16)) return ULYSSES_MISALIGNED;
   const int64_t src_bytes = seq_to_head ? seq_bytes : head_bytes;
   const int64_t dst_bytes = seq_to_head ? head_bytes : seq_bytes;

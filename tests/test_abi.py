@@ -66,6 +66,9 @@ def test_permutation_validation(fn):
     assert fn(A, A + 16) == 5                        # overlapping buffers
     assert fn(A, A, dtype=U.FP32) == 5
     assert fn(A, A + 64 * GB, L=1 << 24, H=1024, P=4) == 3   # 32 GiB and above
+    # sizes whose byte count overflows 64 bits are rejected, not wrapped
+    assert fn(A, A + GB, B=1 << 30, L=1 << 30, H=1, d=64, P=1) == 3
+    assert fn(A, A + GB, B=1 << 30, L=1 << 30, H=1 << 4, P=1 << 4) == 3
 
 
 def fwd(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, L=1024, H=8, d=128, P=4, causal=1,
@@ -229,6 +232,8 @@ def test_kv_layout_validation(fn):
     else:
         assert fn(A, A + head_bytes - 16) == 5       # source (head side) overlaps destination
     assert fn(A, A + GB, B=1 << 20, L=1 << 14, Hkv=1, P=16) == 3   # replicated head tensor past 32 GiB
+    assert fn(A, A + GB, B=1 << 30, L=1 << 30, Hkv=1, d=64, P=1) == 3      # byte counts past 64 bits
+    assert fn(A, A + GB, B=1 << 28, L=1 << 30, Hkv=1, P=1 << 20) == 3
 
 
 def fwd_gqa(q=A, k=A + GB, v=A + 2 * GB, o=A + 3 * GB, lse=A + 4 * GB, B=1, Lq=1024, Lkv=1024, Hq=32, Hkv=8, d=128,
