@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan,
       // dK/dV kernel numbers its work items (nb = batch x K/V heads here)
       const int x = nkb - col / nb;
       nch = (x + ck - 1) / ck;
-      slot = nb * (chunk_prefix(nkb, ck) - chunk_prefix(x, ck)) + (col % nb) * nch;
+      slot = causal_chunk_first(x, col % nb, nkb, nb, ck);
     }
     const int kb = DENSE ? col / nb : col % nb, hb = DENSE ? col % nb : col / nb;
     const int b = hb / Hk, hk = hb - b * Hk;
@@ -847,12 +847,11 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restr
                                                             int Lq, int Hq, int nqb, int nhb, int ck, float scale) {
   constexpr int UNITS = 128 * D / 1024, ROWS = 1024 / D;   // units per block, rows per unit
   const int nunits = nqb * nhb * UNITS;
-  const int sn = CAUSAL ? chunk_prefix(nqb, ck) : 0;
   for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
     const int bi = u / UNITS;                    // blocks longest first, head pairs inner
     const int x = nqb - bi / nhb, hb = bi % nhb;
     const int nch = CAUSAL ? (x + ck - 1) / ck : ck;
-    const int base = CAUSAL ? nhb * (sn - chunk_prefix(x, ck)) + hb * nch : bi * nch;
+    const int base = CAUSAL ? causal_chunk_first(x, hb, nqb, nhb, ck) : bi * nch;
     const int row = (u - bi * UNITS) * ROWS + (int)threadIdx.x / (D / 4);
     const int c4 = ((int)threadIdx.x % (D / 4)) * 4;
     f32x4 acc = f32x4{};

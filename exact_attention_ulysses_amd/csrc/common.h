@@ -38,8 +38,8 @@ __host__ __device__ inline FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-  uint32_t t = __umulhi(n, f.m);
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  const uint32_t t = uint32_t((uint64_t(n) * f.m) >> 32);   // high half of the product (v_mul_hi_u32)
   return uint32_t((uint64_t(t) + n) >> f.s);
 }
 
@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 // when jobs shrink (longest first). Launches round their grid up to whole
 // rounds; workgroups past the last job exit at once.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int xcd_run_job(int bid, int run) {
+__host__ __device__ __forceinline__ int xcd_run_job(int bid, int run) {
   const int x = bid & 7, j = bid >> 3;
   const int round = j / run;
   return 8 * run * round + run * ((round & 1) ? 7 - x : x) + (j - round * run);
@@ -70,7 +70,7 @@ __host__ __device__ inline unsigned xcd_run_grid(long long jobs, int run) {
 // consecutive ranks of one head pair (each XCD then streams the tiles of
 // one head) rather than every head's at once. Returns false past the last
 // job.
-__device__ __forceinline__ bool xcd_run_block(int bid, int run, int nhb, int nranks, int* rank, int* hb) {
+__host__ __device__ __forceinline__ bool xcd_run_block(int bid, int run, int nhb, int nranks, int* rank, int* hb) {
   const int j = xcd_run_job(bid, run);
   const int span = 8 * run;
   if (span % nhb == 0) {
@@ -97,12 +97,20 @@ __host__ __device__ inline int chunk_prefix(int m, int t) {
   return t * a * (a + 1) / 2 + r * (a + 1);
 }
 
+// First work item of block x - 1, head pair hb: the items of the longer
+// blocks x + 1 .. nblk come first (nhb (S(nblk) - S(x)) of them), then the
+// ceil(x / t) parts of each head pair before hb. Reduce kernels read a
+// block's parts from here on.
+__host__ __device__ inline int causal_chunk_first(int x, int hb, int nblk, int nhb, int t) {
+  return nhb * (chunk_prefix(nblk, t) - chunk_prefix(x, t)) + hb * ((x + t - 1) / t);
+}
+
 // Work item i of nhb * S(nblk): block x - 1 (returned as x), head pair hb,
 // part `chunk` of nchunk = ceil(x / t). The items before block x number
 // nhb (S(nblk) - S(x)); x is the smallest block whose predecessors number at
 // most i.
-__device__ inline void causal_chunk_item(int i, int nblk, int nhb, int t, int* x, int* hb, int* chunk,
-                                         int* nchunk) {
+__host__ __device__ inline void causal_chunk_item(int i, int nblk, int nhb, int t, int* x, int* hb, int* chunk,
+                                                  int* nchunk) {
   const int sn = chunk_prefix(nblk, t);
   int lo = 1, hi = nblk;
   while (lo < hi) {
