@@ -530,9 +530,20 @@ def attn_bwd_block_sparse(q, k, v, do, layout, block: int, causal: bool = True):
     return dq, dk, dv
 
 
+def _active_keys(layout_row: np.ndarray, block: int, L: int) -> np.ndarray:
+    """Token indices of the key blocks a layout row marks, ascending. Keys of
+    the other blocks are invisible to the row's queries, so the softmax and
+    every product over them may be formed over these keys alone."""
+    act = np.nonzero(np.asarray(layout_row))[0]
+    if len(act) == 0:
+        return np.empty(0, dtype=np.int64)
+    return np.concatenate([np.arange(jb * block, min(L, (jb + 1) * block), dtype=np.int64) for jb in act])
+
+
 def attn_rows_block_sparse(q, k, v, rows, layout, block: int, causal: bool = True, do=None):
     """Forward (and with dO the dQ row) of selected query rows of one head under a
-    block layout; each row costs O(L d). Returns dict o, lse (and D, dq)."""
+    block layout; each row is formed over the keys of its layout row's active
+    blocks. Returns dict o, lse (and D, dq)."""
     L, d = k.shape
     scale = 1.0 / math.sqrt(d)
     rows = list(rows)
@@ -541,46 +552,79 @@ def attn_rows_block_sparse(q, k, v, rows, layout, block: int, causal: bool = Tru
         out["D"] = np.empty(len(rows))
         out["dq"] = np.zeros((len(rows), d))
     for n, i in enumerate(rows):
-        vis = block_visible(layout[i // block], block, i, i + 1, L, causal)
-        s = (np.asarray(k, dtype=np.float64) @ np.asarray(q[i], dtype=np.float64)) * scale
-        p, lse = _masked_softmax_rows(s[None, :], vis)
+        keys = _active_keys(layout[i // block], block, L)
+        if len(keys) == 0:   # a block row the layout leaves empty: no keys, O = 0, LSE = -inf
+            out["lse"][n] = -np.inf
+            if do is not None:
+                out["D"][n] = 0.0
+            continue
+        vis = (keys <= i) if causal else np.ones(len(keys), bool)
+        kk = np.asarray(k[keys], dtype=np.float64).reshape(len(keys), d)
+        vv = np.asarray(v[keys], dtype=np.float64).reshape(len(keys), d)
+        s = (kk @ np.asarray(q[i], dtype=np.float64)) * scale
+        p, lse = _masked_softmax_rows(s[None, :], vis[None, :])
         out["lse"][n] = lse[0]
-        oi = p[0] @ np.asarray(v, dtype=np.float64)
+        oi = p[0] @ vv
         out["o"][n] = oi
         if do is not None:
             doi = np.asarray(do[i], dtype=np.float64)
             Di = float(doi @ oi)
-            dp = np.asarray(v, dtype=np.float64) @ doi
+            dp = vv @ doi
             out["D"][n] = Di
-            out["dq"][n] = ((p[0] * (dp - Di)) @ np.asarray(k, dtype=np.float64)) * scale
+            out["dq"][n] = ((p[0] * (dp - Di)) @ kk) * scale
     return out
 
 
-def attn_dkv_cols_block_sparse(q, k, v, do, cols, layout, block: int, causal: bool = True):
+def attn_dkv_cols_block_sparse(q, k, v, do, cols, layout, block: int, causal: bool = True,
+                               row_blocks: Optional[Tuple[int, int]] = None, abs_sums: bool = False):
     """dK and dV of selected key columns of one head under a block layout: only
     the block rows whose layout row reaches a selected column's block are
-    formed (each in full, for its LSE and D). Returns (cols, dk, dv)."""
+    formed, each over all keys of its active blocks (for its LSE and D).
+    With row_blocks = (b0, b1) only the terms of query blocks b0 <= bi < b1
+    are summed, so the sums of a partition of the blocks add up to the whole.
+    Returns (cols, dk, dv), and with abs_sums also the sums of the absolute
+    values of the products behind them (as attn_abs_sums_block_sparse_head:
+    |dS| |q| for dK, P |dO| for dV). Test infrastructure."""
     L, d = k.shape
     scale = 1.0 / math.sqrt(d)
     cols = np.asarray(sorted(set(int(c) for c in cols)), dtype=np.int64)
     cblocks = np.unique(cols // block)
     dk = np.zeros((len(cols), d))
     dv = np.zeros((len(cols), d))
-    kk = np.asarray(k, dtype=np.float64)
-    vv = np.asarray(v, dtype=np.float64)
-    for bi, i0 in enumerate(range(0, L, block)):
+    a_dk = np.zeros((len(cols), d))
+    a_dv = np.zeros((len(cols), d))
+    vc = np.asarray(v[cols], dtype=np.float64)
+    nbq = -(-L // block)
+    b0, b1 = (0, nbq) if row_blocks is None else (max(0, int(row_blocks[0])), min(nbq, int(row_blocks[1])))
+    for bi in range(b0, b1):
+        i0 = bi * block
         i1 = min(L, i0 + block)
         if not np.any(np.asarray(layout[bi])[cblocks]) or (causal and i1 - 1 < cols.min()):
             continue
+        keys = _active_keys(layout[bi], block, L)
         qb = np.asarray(q[i0:i1], dtype=np.float64)
         dob = np.asarray(do[i0:i1], dtype=np.float64)
-        vis = block_visible(layout[bi], block, i0, i1, L, causal)
+        kk = np.asarray(k[keys], dtype=np.float64).reshape(len(keys), d)
+        vv = np.asarray(v[keys], dtype=np.float64).reshape(len(keys), d)
+        vis = np.ones((i1 - i0, len(keys)), bool)
+        if causal:
+            vis &= keys[None, :] <= np.arange(i0, i1)[:, None]
         p, _ = _masked_softmax_rows((qb @ kk.T) * scale, vis)
         Db = np.sum(dob * (p @ vv), axis=1)
-        pc = p[:, cols]
-        dsc = pc * (dob @ vv[cols].T - Db[:, None])
+        # probabilities of the selected columns (0 for a column outside the active
+        # blocks; the row block marks at least one block, so keys is not empty)
+        pos = np.minimum(np.searchsorted(keys, cols), len(keys) - 1)
+        present = keys[pos] == cols
+        pc = np.zeros((i1 - i0, len(cols)))
+        pc[:, present] = p[:, pos[present]]
+        dsc = pc * (dob @ vc.T - Db[:, None])
         dk += (dsc.T @ qb) * scale
         dv += pc.T @ dob
+        if abs_sums:
+            a_dk += (np.abs(dsc).T @ np.abs(qb)) * scale
+            a_dv += pc.T @ np.abs(dob)
+    if abs_sums:
+        return cols, dk, dv, a_dk, a_dv
     return cols, dk, dv
 
 

@@ -10,6 +10,16 @@
   1,048,319 keys (a ragged last key tile) on 16 heads, bidirectional, forward
   and backward; every element of O, LSE, dQ, dK and dV of the first and the
   last head (whose rows sit at the highest offsets) against the fp64 oracle.
+* Block layouts at the backward's pair-list limit: G query heads per K/V
+  head times nb query blocks = 8192 listed (query head, query block) pairs
+  in the two global key-block columns (G = 8 at 131,072 tokens; G = 1 at
+  1,048,576 tokens, where query block indices reach 8191), whose chunks take
+  all 512 partial-sum slots; sampled rows and key columns (the global
+  blocks', a window block's, the last block's) against the fp64 oracle. A
+  global column's dK and dV sum up to a million products, each carrying the
+  rounding of P or dS to bf16 before the MFMAs: their elementwise bar adds
+  2^-8 of the oracle's absolute sums of those products (the bound on that
+  rounding), as the random-shape sweep does.
 """
 import gc
 
@@ -19,7 +29,9 @@ import pytest
 import exact_attention_ulysses_amd as U
 import oracle
 
-from gpu_common import LSE_ABS, check_close, to_f64, torch_mod
+from workloads import block_layout, custom
+
+from gpu_common import LSE_ABS, check_close, host_parallel, shared_head_allowed, to_f64, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -114,5 +126,66 @@ def test_attention_at_the_row_offset_limit():
         gc.collect()
         print(f"[limits] head {h} checked", flush=True)
     del q, k, v, do, o, lse, dq, dk, dv, ws
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("L,Hq", [(131072, 8), (1 << 20, 1)])
+def test_block_layout_at_the_pair_list_limit(L, Hq):
+    torch = torch_mod()
+    B, Hkv, d, P, block = 1, 1, 128, 1, U.SPARSE_BLOCK
+    nb, G = L // block, Hq // Hkv
+    assert G * nb == 8192   # the most (query head, query block) pairs a key block's list holds
+    print(f"[limits] block layout L={L} G={G}: {G * nb} pairs per global column", flush=True)
+    lay = block_layout(custom(B, L, Hq, d, 1, causal=True, index=950 + Hq, block=block, window=2, n_global=2,
+                              n_random=1))
+    g = torch.Generator(device="cuda")
+
+    def draw(shape, seed):
+        g.manual_seed(seed)
+        return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    q, do = draw((B, L, Hq, d), 21), draw((B, L, Hq, d), 24)
+    k, v = draw((B, L, Hkv, d), 22), draw((B, L, Hkv, d), 23)
+    layout = torch.from_numpy(lay).to("cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device="cuda")
+    U.ulysses_attn_fwd_block_sparse(q, k, v, o, lse, layout, B, L, Hq, Hkv, d, P, True)
+    dq = torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(U.ulysses_attn_bwd_block_sparse_workspace_bytes(B, L, Hq, Hkv, d, P, True), dtype=torch.uint8,
+                     device="cuda")
+    U.ulysses_attn_bwd_block_sparse(q, k, v, o, do, lse, dq, dk, dv, layout, ws, B, L, Hq, Hkv, d, P, True)
+    torch.cuda.synchronize()
+    print("[limits] block layout device pass done", flush=True)
+    kf, vf = (to_f64(t[0, :, 0].contiguous(), "bf16") for t in (k, v))
+    qf = {h: to_f64(q[0, :, h].contiguous(), "bf16") for h in range(Hq)}
+    dof = {h: to_f64(do[0, :, h].contiguous(), "bf16") for h in range(Hq)}
+    rows = [0, 1, 127, 128, 129, L // 2, L - 129, L - 128, L - 1]
+    for h in sorted({0, Hq - 1}):
+        r = oracle.attn_rows_block_sparse(qf[h], kf, vf, rows, lay[h], block, True, do=dof[h])
+        check_close(f"O rows head {h}", to_f64(o[0, rows, h], "bf16"), r["o"], "bf16", fro=False)
+        check_close(f"dQ rows head {h}", to_f64(dq[0, rows, h], "bf16"), r["dq"], "bf16", fro=False)
+        assert np.max(np.abs(lse[0, h, rows].cpu().numpy() - r["lse"])) <= LSE_ABS["bf16"]
+    # key columns of the two global blocks, a middle block and the last block;
+    # the K/V head's gradient sums its G query heads' columns
+    cols = [0, 1, 127, 128, 255, L // 2 + 3, L - 128, L - 1]
+    # (head, range of query blocks) work items on the host's cores; a head's ranges add up
+    ranges = [(h, (nb * j // 16, nb * (j + 1) // 16)) for h in range(Hq) for j in range(16)]
+    got_parts = host_parallel(lambda it: oracle.attn_dkv_cols_block_sparse(qf[it[0]], kf, vf, dof[it[0]], cols,
+                                                                           lay[it[0]], block, True,
+                                                                           row_blocks=it[1], abs_sums=True)[1:],
+                              ranges)
+    parts = [[sum(p[i] for (h2, _), p in zip(ranges, got_parts) if h2 == h) for i in range(4)] for h in range(Hq)]
+    # the global columns sum a million products each: their bar adds the bound
+    # on rounding dS and P to bf16 before the products, 2^-8 of the absolute sums
+    for name, got, i in (("dK", dk, 0), ("dV", dv, 1)):
+        stack = np.stack([p[i] for p in parts])
+        want = stack.sum(axis=0)
+        abs_sum = sum(p[i + 2] for p in parts)
+        allowed = shared_head_allowed(stack, want, "bf16") if G > 1 else None
+        check_close(f"{name} columns", to_f64(got[0, cols, 0], "bf16"), want, "bf16", fro=False, allowed=allowed,
+                    abs_sum=abs_sum)
+    del q, k, v, do, o, lse, dq, dk, dv, ws, layout
     gc.collect()
     torch.cuda.empty_cache()

@@ -807,6 +807,39 @@ def test_block_sparse_brute_force_and_sampled_rows():
     np.testing.assert_allclose(r["dq"], dq[rows], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_sparse_sampled_functions_cover_every_row_and_column(causal):
+    # the sampled forms (formed over the active blocks' keys) against the full
+    # masked head on a ragged length, a random layout and an emptied block row
+    L, d, block = 45, 6, 8
+    q, k, v, do = (_rand((L, d), s) for s in (90, 91, 92, 93))
+    nb = -(-L // block)
+    lay = _layout(nb, "random", seed=11)
+    lay[3] = 0
+    dq, dk, dv, o, lse, _ = oracle.attn_bwd_block_sparse_head(q, k, v, do, lay, block, causal)
+    r = oracle.attn_rows_block_sparse(q, k, v, range(L), lay, block, causal, do=do)
+    np.testing.assert_allclose(r["o"], o, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(np.isinf(r["lse"]), np.isinf(lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(r["lse"][fin], lse[fin], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["dq"], dq, rtol=0, atol=1e-12)
+    c, dkc, dvc = oracle.attn_dkv_cols_block_sparse(q, k, v, do, range(L), lay, block, causal)
+    np.testing.assert_allclose(dkc, dk[c], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[c], rtol=0, atol=1e-12)
+    # over a partition of the query blocks the parts add up to the whole
+    parts = [oracle.attn_dkv_cols_block_sparse(q, k, v, do, range(L), lay, block, causal, row_blocks=rb)
+             for rb in ((0, 2), (2, 3), (3, nb))]
+    np.testing.assert_allclose(sum(p[1] for p in parts), dk[c], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sum(p[2] for p in parts), dv[c], rtol=0, atol=1e-12)
+    # the absolute sums of the columns' products, as the full head's
+    _, _, _, a_dkc, a_dvc = oracle.attn_dkv_cols_block_sparse(q, k, v, do, range(L), lay, block, causal,
+                                                              abs_sums=True)
+    _, a_dk, a_dv, _ = oracle.attn_abs_sums_block_sparse_head(q, k, v, do, lay, block, causal)
+    np.testing.assert_allclose(a_dkc, a_dk[c], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a_dvc, a_dv[c], rtol=0, atol=1e-12)
+    assert np.all(a_dkc >= np.abs(dkc) - 1e-12) and np.all(a_dvc >= np.abs(dvc) - 1e-12)
+
+
 def test_block_sparse_row_without_keys():
     # a block row the layout leaves empty: zero output, LSE -inf, no gradient flow
     L, d, block = 32, 4, 8
