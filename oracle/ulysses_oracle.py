@@ -397,6 +397,39 @@ def seq_to_head_kv(x: np.ndarray, B: int, L: int, Hkv: int, d: int, P: int) -> n
     return out
 
 
+def seq_to_head_kv_source_rows(B: int, L: int, Hkv: int, P: int) -> np.ndarray:
+    """For every destination row of the K/V head layout, the source row of the
+    seq layout (seq_to_head_kv as index arithmetic). With replication
+    (R = P / Hkv ranks per KV head) destination row (p, b, n, 0) of
+    [P, B, L, 1] takes row (r, b, t, p div R) of [P, B, L/P, Hkv], r = n div
+    (L/P), t = n mod (L/P); without it the map is seq_to_head's."""
+    R = kv_replication(Hkv, P)
+    if R == 1:
+        return seq_to_head_source_rows(B, L, Hkv, P)
+    Lp = L // P
+    p = np.arange(P, dtype=np.int64)[:, None, None]
+    b = np.arange(B, dtype=np.int64)[None, :, None]
+    n = np.arange(L, dtype=np.int64)[None, None, :]
+    r, t = n // Lp, n % Lp
+    return (((r * B + b) * Lp + t) * Hkv + p // R).reshape(-1)
+
+
+def head_to_seq_kv_grad_source_rows(B: int, L: int, Hkv: int, P: int) -> np.ndarray:
+    """[R, rows of the seq layout]: the R head-layout rows whose sum is each
+    destination row of head_to_seq_kv_grad (R = 1: head_to_seq's map).
+    Destination row (r, b, t, h) of [P, B, L/P, Hkv] sums rows
+    (h R + j, b, r (L/P) + t, 0) of [P, B, L, 1], j = 0 .. R-1."""
+    R = kv_replication(Hkv, P)
+    if R == 1:
+        return head_to_seq_source_rows(B, L, Hkv, P)[None, :]
+    Lp = L // P
+    r = np.arange(P, dtype=np.int64)[:, None, None, None]
+    b = np.arange(B, dtype=np.int64)[None, :, None, None]
+    t = np.arange(Lp, dtype=np.int64)[None, None, :, None]
+    h = np.arange(Hkv, dtype=np.int64)[None, None, None, :]
+    return np.stack([(((h * R + j) * B + b) * L + r * Lp + t).reshape(-1) for j in range(R)])
+
+
 def head_to_seq_kv_grad(y: np.ndarray, B: int, L: int, Hkv: int, d: int, P: int) -> np.ndarray:
     """Adjoint of seq_to_head_kv for dK/dV (float64): with replication the R
     copies of a KV head are summed back into its token shards."""

@@ -5,6 +5,11 @@
   every element of seq_to_head against the oracle's row map (the oracle's
   index arithmetic, applied with a device gather), and head_to_seq of the
   result back to the input bit for bit.
+* The K/V layout change at the same limit on its head side (each of 2 K/V
+  heads replicated on 4 of 8 ranks, L = 2^24 - 8): every element against
+  the oracle's row map, and its gradient form (the 4 replicas summed back
+  into their token shards) on every element within the rounding bound of an
+  fp32 sum of 4 terms and one bf16 rounding.
 * Attention at the 32-bit byte-offset limit of one batch entry's rows
   ((Lk + 256) * H_kv * d_h * 2 bytes just below 2^32): 256 queries against
   1,048,319 keys (a ragged last key tile) on 16 heads, bidirectional, forward
@@ -80,6 +85,57 @@ def test_layout_change_at_the_tensor_size_limit():
     torch.cuda.synchronize()
     assert torch.equal(back.view(torch.int16), x.view(torch.int16)), "head_to_seq(seq_to_head(x)) != x"
     del x, y, want, back
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_kv_layout_change_at_the_tensor_size_limit():
+    torch = torch_mod()
+    B, P, Hkv, d = 1, 8, 2, 128
+    R = P // Hkv
+    L = (1 << 24) - 8
+    head_words = P * B * L * d * 2 // 16
+    assert head_words == (1 << 31) - 1024   # the head side is R times the seq side
+    Lp = L // P
+    print(f"[limits] K/V layout change L={L} Hkv={Hkv} P={P}: head side {head_words * 16 / 2**30:.3f} GiB", flush=True)
+    x = _random_bits((P, B, Lp, Hkv, d), 700)
+    y = torch.empty((P, B, L, 1, d), dtype=torch.bfloat16, device="cuda")
+    U.ulysses_seq_to_head_kv(x, y, B, L, Hkv, d, P)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(oracle.seq_to_head_kv_source_rows(B, L, Hkv, P)).to("cuda")
+    xr, yr = x.view(torch.int16).view(-1, d), y.view(torch.int16).view(-1, d)
+    step = 1 << 24
+    for c0 in range(0, rows.numel(), step):
+        assert torch.equal(xr.index_select(0, rows[c0:c0 + step]), yr[c0:c0 + step]), f"rows from {c0}"
+    del x, y, rows, xr, yr
+    gc.collect()
+    torch.cuda.empty_cache()
+    # the gradient form: dY random normal in the head layout, summed back over the replicas
+    g = torch.Generator(device="cuda")
+    dy = torch.empty((P, B, L, 1, d), dtype=torch.bfloat16, device="cuda")
+    for p in range(P):
+        g.manual_seed(710 + p)
+        dy[p].copy_(torch.randn((B, L, 1, d), generator=g, device="cuda", dtype=torch.float32))
+    out = torch.empty((P, B, Lp, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    U.ulysses_head_to_seq_kv_grad(dy, out, B, L, Hkv, d, P)
+    torch.cuda.synchronize()
+    grows = torch.from_numpy(oracle.head_to_seq_kv_grad_source_rows(B, L, Hkv, P)).to("cuda")
+    assert grows.shape[0] == R
+    dyr, outr = dy.view(-1, d), out.view(-1, d)
+    worst = 0.0
+    step = 1 << 22   # rows per fp64 check (4 GiB per operand)
+    for c0 in range(0, grows.shape[1], step):
+        parts = [dyr.index_select(0, grows[j, c0:c0 + step]).double() for j in range(R)]
+        want = sum(parts)
+        err = (R - 1) * 2.0 ** -24 * sum(t.abs() for t in parts)   # fp32 sum of R terms
+        _, e = torch.frexp(want.abs() + err)
+        bar = 0.5 * torch.ldexp(torch.ones_like(want), e - 8) + err   # one bf16 rounding of the sum
+        ratio = ((outr[c0:c0 + step].double() - want).abs() / bar).max().item()
+        worst = max(worst, ratio)
+        assert ratio <= 1.0, f"rows from {c0}: {ratio}"
+        del parts, want, err, e, bar
+    print(f"[limits] K/V gradient form: worst error {worst:.3f} of the bound", flush=True)
+    del dy, out, grows, dyr, outr
     gc.collect()
     torch.cuda.empty_cache()
 

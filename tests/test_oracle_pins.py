@@ -658,6 +658,13 @@ def test_kv_layout_change_by_procedure_and_adjoint(B, L, Hkv, d, P):
     lhs = float(np.sum(oracle.seq_to_head_kv(xf, B, L, Hkv, d, P) * g))
     rhs = float(np.sum(xf * oracle.head_to_seq_kv_grad(g, B, L, Hkv, d, P)))
     assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    # the row maps restate both directions as index arithmetic
+    rows = oracle.seq_to_head_kv_source_rows(B, L, Hkv, P)
+    np.testing.assert_array_equal(x.reshape(-1, d)[rows].reshape(y.shape), y)
+    grows = oracle.head_to_seq_kv_grad_source_rows(B, L, Hkv, P)
+    assert grows.shape[0] == R
+    summed = sum(g.reshape(-1, d)[grows[j]] for j in range(R)).reshape(P, B, L // P, Hkv, d)
+    np.testing.assert_allclose(summed, oracle.head_to_seq_kv_grad(g, B, L, Hkv, d, P), rtol=0, atol=1e-12)
 
 
 @pytest.mark.parametrize("Hq,Hkv,P", [(8, 2, 2), (8, 2, 4), (4, 1, 4), (8, 2, 8)])
