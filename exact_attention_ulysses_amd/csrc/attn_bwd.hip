@@ -868,132 +868,202 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restr
   }
 }
 
-// fp32 dK/dV: one lane per key row.
+// fp32 dK/dV on the fp32 MFMA: workgroup = 4 waves x 32 key rows (128 keys),
+// query tiles of 32 rows (Q, dO, LSE, delta) in LDS. Each wave forms
+// S = Q K^T and dP = dO V^T with keys across lanes (K and V of its keys in
+// registers), so that P and dS = P o (dP - delta) are the B operands of
+// dV^T += dO^T P and dK^T += Q^T dS directly; dO^T and Q^T are read from the
+// row-major tiles in the accumulator's row order. Grouped-query heads: the
+// walk covers the query tiles of the G query heads in turn.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dk, float* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float scale) {
-  constexpr int BQ = 32;
-  __shared__ float Qs[BQ][D];
-  __shared__ float Os[BQ][D];
-  __shared__ float ls[BQ], dls[BQ];
-  const int tid = threadIdx.x;
+    float* __restrict__ dk, float* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
+    float scale) {
+  constexpr int BQ = 32, ST = StrideF32<D>::row, KS = D / 2, DT = D / 32, C4 = D / 4;
+  __shared__ __attribute__((aligned(16))) float Qs[BQ * ST];
+  __shared__ __attribute__((aligned(16))) float Ds[BQ * ST];   // dO rows
+  __shared__ float ls[BQ], dls[BQ];   // LSE (log2 units; +inf past the end) and delta per row
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kb = blockIdx.x / nhb;
   const int hb = blockIdx.x % nhb;         // (batch, key head) pair
   const int b = hb / Hk, hk = hb - b * Hk;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
   const size_t koff = ((size_t)b * Lk * Hk + hk) * D;
-  const int key = kb * 64 + tid;
-  const bool valid = key < Lk;
-  float kv[D], vv[D], dka[D], dva[D];
+  const int kw0 = kb * 128 + 32 * wave, key = kw0 + l32;
+
+  // K^T and V^T as B operands: step t holds K[key][2t + hl]
+  float kf[KS], vf[KS];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    kv[e] = valid ? k[koff + (size_t)key * rsk + e] : 0.f;
-    vv[e] = valid ? v[koff + (size_t)key * rsk + e] : 0.f;
-    dka[e] = 0.f;
-    dva[e] = 0.f;
+  for (int t = 0; t < KS; ++t) {
+    kf[t] = key < Lk ? k[koff + (size_t)key * rsk + 2 * t + hl] : 0.f;
+    vf[t] = key < Lk ? v[koff + (size_t)key * rsk + 2 * t + hl] : 0.f;
   }
-  const int qstart = CAUSAL ? kb * 64 : 0;
+  f32x16 dkacc[DT], dvacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dkacc[dt] = f32x16{};
+    dvacc[dt] = f32x16{};
+  }
+  const int qstart = CAUSAL ? kb * 128 : 0;   // causal: no earlier query sees a key of this block
   for (int g = 0; g < G; ++g) {
     const int h = hk * G + g;
     const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
     const size_t loff = ((size_t)b * Hq + h) * Lq;
     for (int q0 = qstart; q0 < Lq; q0 += BQ) {
       __syncthreads();
-      for (int c = tid; c < BQ * D; c += 64) {
-        const int r = c / D, e = c % D, qi = q0 + r;
-        Qs[r][e] = qi < Lq ? q[qoff + (size_t)qi * rsq + e] : 0.f;
-        Os[r][e] = qi < Lq ? d_o[qoff + (size_t)qi * rsq + e] : 0.f;
+      for (int c = tid; c < BQ * C4; c += 256) {
+        const int r = c / C4, e = (c - r * C4) * 4, qi = q0 + r;
+        f32x4 qv = f32x4{}, dv4 = f32x4{};
+        if (qi < Lq) {
+          qv = *reinterpret_cast<const f32x4*>(q + qoff + (size_t)qi * rsq + e);
+          dv4 = *reinterpret_cast<const f32x4*>(d_o + qoff + (size_t)qi * rsq + e);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Qs[r * ST + e + i] = qv[i];
+          Ds[r * ST + e + i] = dv4[i];
+        }
       }
       if (tid < BQ) {
         const int qi = q0 + tid;
-        ls[tid] = qi < Lq ? lse[loff + qi] : 0.f;
+        ls[tid] = qi < Lq ? lse[loff + qi] * kLog2e : INFINITY;
         dls[tid] = qi < Lq ? delta[loff + qi] : 0.f;
       }
       __syncthreads();
-      const int rn = min(BQ, Lq - q0);
-      for (int r = 0; r < rn; ++r) {
-        if (CAUSAL && q0 + r < key) continue;
-        float s = 0.f, dp = 0.f;
+      if (CAUSAL && q0 + BQ - 1 < kw0) continue;   // every query of the tile before this wave's keys
+      f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int e = 0; e < D; ++e) {
-          s = fmaf(Qs[r][e], kv[e], s);
-          dp = fmaf(Os[r][e], vv[e], dp);
-        }
-        const float p = expf(s * scale - ls[r]);
-        const float ds = p * (dp - dls[r]);
+      for (int t = 0; t < KS; ++t) {
+        sc = mfma32_f32(Qs[l32 * ST + 2 * t + hl], kf[t], sc);
+        dp = mfma32_f32(Ds[l32 * ST + 2 * t + hl], vf[t], dp);
+      }
+      // element e: query row q0 + kslot_row(e), this lane's key
 #pragma unroll
-        for (int e = 0; e < D; ++e) {
-          dva[e] = fmaf(p, Os[r][e], dva[e]);
-          dka[e] = fmaf(ds, Qs[r][e], dka[e]);
+      for (int e = 0; e < 16; ++e) {
+        const int r = kslot_row(e, lane);
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, -ls[r]));   // 0 past the end (LSE +inf)
+        if (CAUSAL && key > q0 + r) p = 0.f;
+        sc[e] = p;
+        dp[e] = p * (dp[e] - dls[r]);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = kslot_row(j, lane);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dvacc[dt] = mfma32_f32(Ds[r * ST + 32 * dt + l32], sc[j], dvacc[dt]);
+          dkacc[dt] = mfma32_f32(Qs[r * ST + 32 * dt + l32], dp[j], dkacc[dt]);
         }
       }
     }
   }
-  if (valid) {
+  if (key < Lk) {
+    float* dkrow = dk + koff + (size_t)key * rsk;
+    float* dvrow = dv + koff + (size_t)key * rsk;
 #pragma unroll
-    for (int e = 0; e < D; ++e) {
-      dk[koff + (size_t)key * rsk + e] = dka[e] * scale;
-      dv[koff + (size_t)key * rsk + e] = dva[e];
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 wk, wv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wk[i] = dkacc[dt][4 * a + i] * scale;
+          wv[i] = dvacc[dt][4 * a + i];
+        }
+        *reinterpret_cast<f32x4*>(dkrow + 32 * dt + 8 * a + 4 * hl) = wk;
+        *reinterpret_cast<f32x4*>(dvrow + 32 * dt + 8 * a + 4 * hl) = wv;
+      }
     }
   }
 }
 
-// fp32 dQ: one lane per query row.
+// fp32 dQ on the fp32 MFMA: workgroup = 4 waves x 32 query rows, key tiles of
+// 32 in LDS; S^T = K Q^T and dP^T = V dO^T (queries across lanes, Q and dO in
+// registers), then dQ^T += K^T dS^T with dS^T as the B operand.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dq_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float scale) {
-  constexpr int BN = 32;
-  __shared__ float Ks[BN][D];
-  __shared__ float Vs[BN][D];
-  const int tid = threadIdx.x;
-  const int qb = nqb - 1 - (int)blockIdx.x / nhb;
+    float* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale) {
+  constexpr int BN = 32, ST = StrideF32<D>::row, KS = D / 2, DT = D / 32, C4 = D / 4;
+  __shared__ __attribute__((aligned(16))) float Ks[BN * ST];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * ST];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = nqb - 1 - (int)blockIdx.x / nhb;   // longest rows first
   const int hb = blockIdx.x % nhb;
   const int b = hb / Hq, h = hb - b * Hq;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
   const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
   const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
-  const int qrow = qb * 64 + tid;
-  const bool valid = qrow < Lq;
-  float qv[D], dov[D], dqa[D];
+  const int q0 = qb * 128, qw0 = q0 + 32 * wave, qrow = qw0 + l32;
+  const bool rv = qrow < Lq;
+
+  float qf[KS], df[KS];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = valid ? q[qoff + (size_t)qrow * rsq + e] : 0.f;
-    dov[e] = valid ? d_o[qoff + (size_t)qrow * rsq + e] : 0.f;
-    dqa[e] = 0.f;
+  for (int t = 0; t < KS; ++t) {
+    qf[t] = rv ? q[qoff + (size_t)qrow * rsq + 2 * t + hl] : 0.f;
+    df[t] = rv ? d_o[qoff + (size_t)qrow * rsq + 2 * t + hl] : 0.f;
   }
-  const float l_i = valid ? lse[(size_t)hb * Lq + qrow] : 0.f;
-  const float d_i = valid ? delta[(size_t)hb * Lq + qrow] : 0.f;
-  const int kend = CAUSAL ? min(Lk, qb * 64 + 64) : Lk;
+  const float l2 = rv ? lse[(size_t)hb * Lq + qrow] * kLog2e : INFINITY;   // rows past the end: P = 0
+  const float dl = rv ? delta[(size_t)hb * Lq + qrow] : 0.f;
+  f32x16 dqacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dqacc[dt] = f32x16{};
+
+  const int kend = CAUSAL ? min(Lk, q0 + 128) : Lk;
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
-    for (int c = tid; c < BN * D; c += 64) {
-      const int r = c / D, e = c % D, kk = k0 + r;
-      Ks[r][e] = kk < Lk ? k[koff + (size_t)kk * rsk + e] : 0.f;
-      Vs[r][e] = kk < Lk ? v[koff + (size_t)kk * rsk + e] : 0.f;
+    for (int c = tid; c < BN * C4; c += 256) {
+      const int r = c / C4, e = (c - r * C4) * 4, kk = k0 + r;
+      f32x4 kv = f32x4{}, vv = f32x4{};
+      if (kk < Lk) {
+        kv = *reinterpret_cast<const f32x4*>(k + koff + (size_t)kk * rsk + e);
+        vv = *reinterpret_cast<const f32x4*>(v + koff + (size_t)kk * rsk + e);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Ks[r * ST + e + i] = kv[i];
+        Vs[r * ST + e + i] = vv[i];
+      }
     }
     __syncthreads();
-    const int jn = min(BN, Lk - k0);
-    for (int j = 0; j < jn; ++j) {
-      if (CAUSAL && k0 + j > qrow) break;
-      float s = 0.f, dp = 0.f;
+    if (CAUSAL && k0 > qw0 + 31) continue;   // every key of the tile above this wave's rows
+    f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int e = 0; e < D; ++e) {
-        s = fmaf(qv[e], Ks[j][e], s);
-        dp = fmaf(dov[e], Vs[j][e], dp);
-      }
-      const float p = expf(s * scale - l_i);
-      const float ds = p * (dp - d_i);
+    for (int t = 0; t < KS; ++t) {
+      sc = mfma32_f32(Ks[l32 * ST + 2 * t + hl], qf[t], sc);
+      dp = mfma32_f32(Vs[l32 * ST + 2 * t + hl], df[t], dp);
+    }
 #pragma unroll
-      for (int e = 0; e < D; ++e) dqa[e] = fmaf(ds, Ks[j][e], dqa[e]);
+    for (int e = 0; e < 16; ++e) {
+      const int kk = k0 + kslot_row(e, lane);
+      float p = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, -l2));
+      if ((CAUSAL && kk > qrow) || kk >= Lk) p = 0.f;
+      sc[e] = p * (dp[e] - dl);   // dS^T
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kr = kslot_row(j, lane);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dqacc[dt] = mfma32_f32(Ks[kr * ST + 32 * dt + l32], sc[j], dqacc[dt]);
     }
   }
-  if (valid) {
+  if (rv) {
+    float* row = dq + qoff + (size_t)qrow * rsq;
 #pragma unroll
-    for (int e = 0; e < D; ++e) dq[qoff + (size_t)qrow * rsq + e] = dqa[e] * scale;
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = dqacc[dt][4 * a + i] * scale;
+        *reinterpret_cast<f32x4*>(row + 32 * dt + 8 * a + 4 * hl) = w;
+      }
+    }
   }
 }
 
@@ -1233,16 +1303,17 @@ hipError_t bwd_f32(const float* q, const float* k, const float* v, const float* 
   if (e != hipSuccess) return e;
   const int G = s.Hq / s.Hk;
   const float scale = 1.f / sqrtf((float)D);
+  const float sl2 = kLog2e * scale;
   const int nkhb = s.B * s.Hk;
-  const int nkb = (s.Lk + 63) / 64;
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)nkb * nkhb), dim3(64), 0, stream, q, k, v,
-                     d_o, lse, delta, dk, dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, scale);
+  const int nkb = (s.Lk + 127) / 128;
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)nkb * nkhb), dim3(256), 0, stream, q, k, v,
+                     d_o, lse, delta, dk, dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nhb = s.B * s.Hq;
-  const int nqb = (s.Lq + 63) / 64;
-  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(64), 0, stream, q, k, v,
-                     d_o, lse, delta, dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, scale);
+  const int nqb = (s.Lq + 127) / 128;
+  hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream, q, k, v,
+                     d_o, lse, delta, dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale);
   return hipGetLastError();
 }
 

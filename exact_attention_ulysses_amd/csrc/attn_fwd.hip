@@ -34,8 +34,8 @@
 // Block layouts (paper-graph summary, section 3.4 and Figs 6-7, "blocked
 //   sparse attention"): the workgroup of a query block visits only the key
 //   blocks its layout row marks, found with a 64-lane ballot over the row.
-// fp32 path: one lane per query row, K/V tiles in LDS, plain FMAs (used for
-//   the small fp32 workloads; precision reference for the tests).
+// fp32 path: the same shape on the fp32 MFMA (v_mfma_f32_32x32x2_f32), 4 waves
+//   x 32 query rows, key tiles of 32 (attn_fwd_f32_kernel).
 #include <math.h>
 
 #include <type_traits>
@@ -653,65 +653,109 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   }
 }
 
-// fp32: one lane per query row.
+// fp32 on the fp32 MFMA: workgroup = 4 waves x 32 query rows, key tiles of
+// 32 in LDS. Each wave forms S^T = K Q^T (keys down the accumulator rows,
+// queries across lanes; Q^T in registers) and O^T += V^T P^T with the score
+// registers as the B operand, as the bf16 kernels do, with a running row
+// maximum and sum.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
+__global__ __launch_bounds__(256, 1) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb,
-    float scale) {
-  constexpr int BN = 32;
-  __shared__ float Ks[BN][D];
-  __shared__ float Vs[BN][D];
-  const int tid = threadIdx.x;
-  const int qb = nqb - 1 - (int)blockIdx.x / nhb;
+    float sl2) {
+  constexpr int BN = 32, ST = StrideF32<D>::row, KS = D / 2, DT = D / 32, C4 = D / 4;
+  __shared__ __attribute__((aligned(16))) float Ks[BN * ST];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * ST];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = nqb - 1 - (int)blockIdx.x / nhb;   // longest rows first
   const int hb = blockIdx.x % nhb;
   const int b = hb / Hq, h = hb - b * Hq;
   const size_t rsq = (size_t)Hq * D, rsk = (size_t)Hk * D;
   const size_t qoff = ((size_t)b * Lq * Hq + h) * D;
   const size_t koff = ((size_t)b * Lk * Hk + h / G) * D;
-  const int qrow = qb * 64 + tid;
-  const bool valid = qrow < Lq;
+  const int q0 = qb * 128, qw0 = q0 + 32 * wave, qrow = qw0 + l32;
 
-  float qv[D], ov[D];
+  // Q^T as the B operand: step t holds Q[qrow][2t + hl]
+  float qf[KS];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = valid ? q[qoff + (size_t)qrow * rsq + e] * scale : 0.f;
-    ov[e] = 0.f;
-  }
-  float m = -INFINITY, l = 0.f;
-  const int kend = CAUSAL ? min(Lk, qb * 64 + 64) : Lk;
+  for (int t = 0; t < KS; ++t) qf[t] = qrow < Lq ? q[qoff + (size_t)qrow * rsq + 2 * t + hl] : 0.f;
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  // running maximum in log2 units and this lane's share of the running sum
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = CAUSAL ? min(Lk, q0 + 128) : Lk;
   for (int k0 = 0; k0 < kend; k0 += BN) {
     __syncthreads();
-    for (int c = tid; c < BN * D; c += 64) {
-      const int r = c / D, e = c % D, key = k0 + r;
-      Ks[r][e] = key < Lk ? k[koff + (size_t)key * rsk + e] : 0.f;
-      Vs[r][e] = key < Lk ? v[koff + (size_t)key * rsk + e] : 0.f;
+    for (int c = tid; c < BN * C4; c += 256) {
+      const int r = c / C4, e = (c - r * C4) * 4, key = k0 + r;
+      f32x4 kv = f32x4{}, vv = f32x4{};
+      if (key < Lk) {
+        kv = *reinterpret_cast<const f32x4*>(k + koff + (size_t)key * rsk + e);
+        vv = *reinterpret_cast<const f32x4*>(v + koff + (size_t)key * rsk + e);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        Ks[r * ST + e + i] = kv[i];
+        Vs[r * ST + e + i] = vv[i];
+      }
     }
     __syncthreads();
-    const int jn = min(BN, Lk - k0);
-    for (int j = 0; j < jn; ++j) {
-      if (CAUSAL && k0 + j > qrow) break;
-      float s = 0.f;
+    if (CAUSAL && k0 > qw0 + 31) continue;   // every key of the tile above this wave's rows
+    f32x16 sc = f32x16{};
 #pragma unroll
-      for (int e = 0; e < D; ++e) s = fmaf(qv[e], Ks[j][e], s);
-      if (s > m) {
-        const float c = expf(m - s);
-        l *= c;
+    for (int t = 0; t < KS; ++t) sc = mfma32_f32(Ks[l32 * ST + 2 * t + hl], qf[t], sc);
+    if (CAUSAL ? (k0 + BN - 1 > qw0) : (k0 + BN > Lk)) {
 #pragma unroll
-        for (int e = 0; e < D; ++e) ov[e] *= c;
-        m = s;
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + kslot_row(e, lane);
+        if ((CAUSAL && key > qrow) || key >= Lk) sc[e] = -INFINITY;
       }
-      const float p = expf(s - m);
-      l += p;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < D; ++e) ov[e] = fmaf(p, Vs[j][e], ov[e]);
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // finite from the first tile on: key 0 is visible to every row
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, -m_run));
+      sc[e] = p;
+      rs += p;
+    }
+    l_run += rs;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int kr = kslot_row(j, lane);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32_f32(Vs[kr * ST + 32 * dt + l32], sc[j], oacc[dt]);
     }
   }
-  if (valid) {
-    const float inv = 1.f / l;
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow < Lq) {
+    const float inv = 1.f / l_tot;
+    float* orow = o + qoff + (size_t)qrow * rsq;
 #pragma unroll
-    for (int e = 0; e < D; ++e) o[qoff + (size_t)qrow * rsq + e] = ov[e] * inv;
-    lse[(size_t)hb * Lq + qrow] = m + logf(l);
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = oacc[dt][4 * a + i] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * a + 4 * hl) = w;
+      }
+    }
+    if (hl == 0) lse[(size_t)hb * Lq + qrow] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
@@ -771,11 +815,11 @@ hipError_t fwd_bf16(const void* q, const void* k, const void* v, void* o, float*
 template <int D, bool CAUSAL>
 hipError_t fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, const AttnShape& s,
                    hipStream_t stream) {
-  const int nqb = (s.Lq + 63) / 64;
+  const int nqb = (s.Lq + 127) / 128;
   const int nhb = s.B * s.Hq;
-  const float scale = 1.f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(64), 0, stream, q, k, v,
-                     o, lse, s.Lq, s.Lk, s.Hq, s.Hk, s.Hq / s.Hk, nqb, nhb, scale);
+  const float sl2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)nqb * nhb), dim3(256), 0, stream, q, k, v,
+                     o, lse, s.Lq, s.Lk, s.Hq, s.Hk, s.Hq / s.Hk, nqb, nhb, sl2);
   return hipGetLastError();
 }
 

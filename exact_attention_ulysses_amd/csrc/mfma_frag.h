@@ -55,6 +55,23 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// fp32 operands (v_mfma_f32_32x32x2_f32): lane l holds A[l % 32][l / 32] and
+// B[l / 32][l % 32]; the accumulator layout is the one above. The fp32 kernels
+// pair accumulator rows 8 * (j / 4) + j % 4 (lanes 0-31) and the same + 4
+// (lanes 32-63) as the two k slots of step j, so that element j of a 32x32
+// accumulator is a ready B operand; the A operand of that step reads the same
+// two rows of its LDS tile (kslot_row).
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int kslot_row(int j, int lane) { return 8 * (j >> 2) + (j & 3) + 4 * (lane >> 5); }
+
+// fp32 LDS tiles: rows of D + 2 floats, so that the 64 lanes of a read of two
+// adjacent columns over 32 rows (an operand whose k runs along a row) fall in
+// 64 different banks.
+template <int D> struct StrideF32 { static constexpr int row = D + 2; };
+
 // k along a row: lane l gets T[row0 + l % 32][col0 + 8 * (l / 32) + i].
 template <int STRIDE>
 __device__ __forceinline__ bf16x8 frag_row(const __bf16* t, int row0, int col0, int lane) {
