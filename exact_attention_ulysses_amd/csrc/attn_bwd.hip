@@ -870,18 +870,24 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restr
 
 // fp32 dK/dV on the fp32 MFMA: workgroup = 4 waves x 32 key rows (128 keys),
 // query tiles of 32 rows (Q, dO, LSE, delta) in LDS. Each wave forms
-// S = Q K^T and dP = dO V^T with keys across lanes (K and V of its keys in
-// registers), so that P and dS = P o (dP - delta) are the B operands of
-// dV^T += dO^T P and dK^T += Q^T dS directly; dO^T and Q^T are read from the
-// row-major tiles in the accumulator's row order. Grouped-query heads: the
-// walk covers the query tiles of the G query heads in turn.
-template <int D, bool CAUSAL>
+// S = Q K^T (and for dK dP = dO V^T) with keys across lanes, K and V of its
+// keys in registers, so that P and dS = P o (dP - delta) are the B operands
+// of dV^T += dO^T P and dK^T += Q^T dS directly; dO^T and Q^T are read from
+// the row-major tiles in the accumulator's row order. Grouped-query heads:
+// the walk covers the query tiles of the G query heads in turn. dK and dV
+// sum over every query, which with few keys means long sums of sizeable
+// terms: each tile's 16 MFMA steps accumulate in fp32 from zero and the tile
+// is added to fp64 running sums, so the result carries the rounding of the
+// small tile sums and one final rounding. The fp64 sums of both outputs do
+// not fit the registers at once: the kernel runs once for dV (WHICH = 0,
+// no dP) and once for dK (WHICH = 1).
+template <int D, bool CAUSAL, int WHICH>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dk, float* __restrict__ dv, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2,
-    float scale) {
+    float* __restrict__ out, int Lq, int Lk, int Hq, int Hk, int G, int nhb, float sl2, float scale) {
   constexpr int BQ = 32, ST = StrideF32<D>::row, KS = D / 2, DT = D / 32, C4 = D / 4;
+  constexpr bool DK = WHICH == 1;
   __shared__ __attribute__((aligned(16))) float Qs[BQ * ST];
   __shared__ __attribute__((aligned(16))) float Ds[BQ * ST];   // dO rows
   __shared__ float ls[BQ], dls[BQ];   // LSE (log2 units; +inf past the end) and delta per row
@@ -894,18 +900,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(
   const size_t koff = ((size_t)b * Lk * Hk + hk) * D;
   const int kw0 = kb * 128 + 32 * wave, key = kw0 + l32;
 
-  // K^T and V^T as B operands: step t holds K[key][2t + hl]
-  float kf[KS], vf[KS];
+  // K^T (and V^T) as B operands: step t holds K[key][2t + hl]
+  float kf[KS], vf[DK ? KS : 1];
 #pragma unroll
   for (int t = 0; t < KS; ++t) {
     kf[t] = key < Lk ? k[koff + (size_t)key * rsk + 2 * t + hl] : 0.f;
-    vf[t] = key < Lk ? v[koff + (size_t)key * rsk + 2 * t + hl] : 0.f;
+    if constexpr (DK) vf[t] = key < Lk ? v[koff + (size_t)key * rsk + 2 * t + hl] : 0.f;
   }
-  f32x16 dkacc[DT], dvacc[DT];
+  double sum[DT][16];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    dkacc[dt] = f32x16{};
-    dvacc[dt] = f32x16{};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum[dt][e] = 0.0;
   }
   const int qstart = CAUSAL ? kb * 128 : 0;   // causal: no earlier query sees a key of this block
   for (int g = 0; g < G; ++g) {
@@ -938,7 +944,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         sc = mfma32_f32(Qs[l32 * ST + 2 * t + hl], kf[t], sc);
-        dp = mfma32_f32(Ds[l32 * ST + 2 * t + hl], vf[t], dp);
+        if constexpr (DK) dp = mfma32_f32(Ds[l32 * ST + 2 * t + hl], vf[t], dp);
       }
       // element e: query row q0 + kslot_row(e), this lane's key
 #pragma unroll
@@ -946,35 +952,36 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_f32_kernel(
         const int r = kslot_row(e, lane);
         float p = __builtin_amdgcn_exp2f(fmaf(sc[e], sl2, -ls[r]));   // 0 past the end (LSE +inf)
         if (CAUSAL && key > q0 + r) p = 0.f;
-        sc[e] = p;
-        dp[e] = p * (dp[e] - dls[r]);
+        sc[e] = DK ? p * (dp[e] - dls[r]) : p;   // dS or P
       }
+      f32x16 acc[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int r = kslot_row(j, lane);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dvacc[dt] = mfma32_f32(Ds[r * ST + 32 * dt + l32], sc[j], dvacc[dt]);
-          dkacc[dt] = mfma32_f32(Qs[r * ST + 32 * dt + l32], dp[j], dkacc[dt]);
-        }
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = mfma32_f32(DK ? Qs[r * ST + 32 * dt + l32] : Ds[r * ST + 32 * dt + l32], sc[j], acc[dt]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum[dt][e] += (double)acc[dt][e];
       }
     }
   }
   if (key < Lk) {
-    float* dkrow = dk + koff + (size_t)key * rsk;
-    float* dvrow = dv + koff + (size_t)key * rsk;
+    float* row = out + koff + (size_t)key * rsk;
+    const double sc = DK ? (double)scale : 1.0;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        f32x4 wk, wv;
+        f32x4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wk[i] = dkacc[dt][4 * a + i] * scale;
-          wv[i] = dvacc[dt][4 * a + i];
-        }
-        *reinterpret_cast<f32x4*>(dkrow + 32 * dt + 8 * a + 4 * hl) = wk;
-        *reinterpret_cast<f32x4*>(dvrow + 32 * dt + 8 * a + 4 * hl) = wv;
+        for (int i = 0; i < 4; ++i) w[i] = (float)(sum[dt][4 * a + i] * sc);
+        *reinterpret_cast<f32x4*>(row + 32 * dt + 8 * a + 4 * hl) = w;
       }
     }
   }
@@ -1306,8 +1313,12 @@ hipError_t bwd_f32(const float* q, const float* k, const float* v, const float* 
   const float sl2 = kLog2e * scale;
   const int nkhb = s.B * s.Hk;
   const int nkb = (s.Lk + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)nkb * nkhb), dim3(256), 0, stream, q, k, v,
-                     d_o, lse, delta, dk, dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale);
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, 0>), dim3((unsigned)nkb * nkhb), dim3(256), 0, stream, q, k,
+                     v, d_o, lse, delta, dv, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, CAUSAL, 1>), dim3((unsigned)nkb * nkhb), dim3(256), 0, stream, q, k,
+                     v, d_o, lse, delta, dk, s.Lq, s.Lk, s.Hq, s.Hk, G, nkhb, sl2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nhb = s.B * s.Hq;
