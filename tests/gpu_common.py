@@ -45,11 +45,6 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 8)
 
 
-def fp32_ulp(x: np.ndarray) -> np.ndarray:
-    """Spacing of fp32 numbers at |x| (24 significant bits): 2^(e-24) for |x| in [2^(e-1), 2^e)."""
-    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
-    return np.ldexp(1.0, e - 24)
-
 
 # every comparison check_close made in this process, for the end-of-run summary
 RECORDS = []
