@@ -45,7 +45,6 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, e - 8)
 
 
-
 # every comparison check_close made in this process, for the end-of-run summary
 RECORDS = []
 
