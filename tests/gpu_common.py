@@ -64,7 +64,7 @@ def check_close(name, got, want, dtype, max_abs=None, rel_fro=None, fro=True, al
     probabilities (or dS) to bf16 before they enter the products, from the
     oracle's absolute sums (oracle.attn_abs_sums_head).
 
-    The returned stats always carry the raw figures beside the verdict:
+    The returned stats always carry the raw figures beside the pass/fail result:
     max_abs, n_over_flat (elements more than 1e-2 (bf16) or 1e-5 (fp32)
     off), and max_err_over_unwidened (the worst error over max(1e-2, ulp),
     or over 1e-5) next to max_err_over_allowed (over the bar the test
