@@ -13,12 +13,12 @@
 // so every output element is written once, without atomics, and results are
 // bitwise reproducible; the price is that S and dP are formed twice.
 //
-// bf16 dK/dV kernel: workgroup = 4 producer/consumer wave pairs x 32 key
-//   rows; K and V of a pair's keys stay in the producer's registers; query
-//   tiles of 64 rows (Q, dO, lse, delta) are staged through LDS. S = Q K^T
-//   and dP = dO V^T put keys across lanes, so the accumulators become the B
-//   operands of dV^T += dO^T P and dK^T += Q^T dS directly; dO^T and Q^T are
-//   read transposed from LDS.
+// bf16 dK/dV kernel: workgroup = 4 producer waves x 32 key rows and 4
+//   consumer waves (dV or dK of 64 keys each); K and V of a producer's keys
+//   stay in its registers; query tiles of 64 rows (Q, dO, lse, delta) are
+//   staged through LDS. S = Q K^T and dP = dO V^T put keys across lanes, so
+//   the accumulators become the B operands of dV^T += dO^T P and
+//   dK^T += Q^T dS directly; dO^T and Q^T are read transposed from LDS.
 // bf16 dQ kernel: workgroup = 4 waves x 32 query rows; the forward kernel's
 //   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
 //   Launches of a few hundred query blocks use 8 waves per block instead,
@@ -227,18 +227,21 @@ __global__ __launch_bounds__(256) void bwd_sparse_reduce_kernel(SparsePlan plan,
   }
 }
 
-// dK/dV as producer/consumer wave pairs. A workgroup owns 128 keys and has 8
-// waves: producer wave w (0..3) and consumer wave w+4 share keys 32w..32w+31
-// and, with the usual in-order placement of a workgroup's waves on the four
-// SIMDs, one SIMD. For each 64-row query tile the producer forms S = Q K^T and
-// dP = dO V^T (K and V of its keys stay in its registers), the probabilities
-// P and dS = P o (dP - delta), and writes both as bf16 MFMA operands to LDS;
-// one tile later its consumer reads them and accumulates dV^T += dO^T P and
-// dK^T += Q^T dS. Neither role needs more than 256 registers, so the pair
-// shares a SIMD and the producer's exponentials and products run while the
-// consumer's MFMAs do. Tiles are double buffered; each step ends with two
-// barriers (hand-over, then the staging of the next tile, which producers
-// (dO) and consumers (Q) share).
+// dK/dV as producer and consumer waves. A workgroup owns 128 keys and has 8
+// waves: producer wave w (0..3) owns keys 32w..32w+31; consumer wave 4 + c
+// accumulates one product, dV (c even) or dK (c odd), for the 64 keys of
+// producers 2 (c / 2) and 2 (c / 2) + 1. For each 64-row query tile a
+// producer forms S = Q K^T and dP = dO V^T (K and V of its keys stay in its
+// registers), the probabilities P and dS = P o (dP - delta), and writes both
+// as bf16 MFMA operands to LDS; one tile later the consumers read them and
+// accumulate dV^T += dO^T P or dK^T += Q^T dS, each transposed dO^T or Q^T
+// fragment they read from LDS feeding the MFMAs of both 32-key halves.
+// Neither role needs more than 256 registers, so a producer and a consumer
+// share each SIMD (in-order placement of a workgroup's waves) and the
+// producer's exponentials and products run while the consumer's MFMAs do.
+// Tiles are double buffered; each step ends with two barriers (hand-over,
+// then the staging of the next tile, which producers (dO) and consumers (Q)
+// share).
 // SPLIT (dense launches of few key blocks): workgroup 2c + h walks half h of
 // key-block column c's query tiles and leaves unscaled fp32 partial sums in
 // slot 2c + h, which the reduce kernel adds in order; with ck > 0 (causal)
@@ -503,26 +506,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
       __syncthreads();  // tile s+1 staged
     }
   } else {
-    // ---------------- consumer: dV, dK ----------------
-    f32x16 dkacc[DT], dvacc[DT];
+    // ---------------- consumer: dV or dK of 64 keys ----------------
+    // consumer wave c (c = wave - 4) takes the keys of producers 2 (c / 2) and
+    // 2 (c / 2) + 1 and one product: dV^T += dO^T P (c even) or dK^T += Q^T dS
+    // (c odd), so every transposed dO^T or Q^T fragment it reads from LDS
+    // feeds two MFMAs, one per 32-key half.
+    const int cw = wave - 4, kp = cw >> 1, role = cw & 1;
+    f32x16 acc[2][DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      dkacc[dt] = f32x16{};
-      dvacc[dt] = f32x16{};
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[h][dt] = f32x16{};
     }
     for (int s = 0; s <= nsteps; ++s) {
       if (s >= 1) {
         const int prev = (s - 1) & 1;
-        const __bf16* Qc = Qs[prev];
-        const __bf16* Dc = Ds[prev];
+        const __bf16* Tc = role ? Qs[prev] : Ds[prev];
 #pragma unroll
         for (int uc = 0; uc < 4; ++uc) {
-          const bf16x8 pf = hand[prev][pw][0][uc][lane];
-          const bf16x8 dsf = hand[prev][pw][1][uc][lane];
+          const bf16x8 b0 = hand[prev][2 * kp][role][uc][lane];
+          const bf16x8 b1 = hand[prev][2 * kp + 1][role][uc][lane];
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            dvacc[dt] = mfma32(frag_col<ST>(Dc, 16 * uc, 32 * dt, lane), pf, dvacc[dt]);
-            dkacc[dt] = mfma32(frag_col<ST>(Qc, 16 * uc, 32 * dt, lane), dsf, dkacc[dt]);
+            const bf16x8 a = frag_col<ST>(Tc, 16 * uc, 32 * dt, lane);
+            acc[0][dt] = mfma32(a, b0, acc[0][dt]);
+            acc[1][dt] = mfma32(a, b1, acc[1][dt]);
           }
         }
       }
@@ -534,31 +542,35 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
     if ((SPARSE && nchunk > 1) || SPLIT) {
       // one chunk of a split column: unscaled fp32 partial sums, [dK | dV][128 keys][D],
       // summed in chunk order by the reduce kernel
-      float* part = plan.partials + (size_t)(slot + chunk) * 2 * 128 * D;
-      const int kr = key - kb * 128;
+      float* part = plan.partials + ((size_t)(slot + chunk) * 2 * 128 + (role ? 0 : 128)) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int h = 0; h < 2; ++h) {
+        const int kr = 64 * kp + 32 * h + l32;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          f32x4 k4, v4;
+        for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            k4[i] = dkacc[dt][4 * a + i];
-            v4[i] = dvacc[dt][4 * a + i];
+          for (int a = 0; a < 4; ++a) {
+            f32x4 x4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x4[i] = acc[h][dt][4 * a + i];
+            *reinterpret_cast<f32x4*>(part + (size_t)kr * D + 32 * dt + 8 * a + 4 * hl) = x4;
           }
-          *reinterpret_cast<f32x4*>(part + (size_t)kr * D + 32 * dt + 8 * a + 4 * hl) = k4;
-          *reinterpret_cast<f32x4*>(part + (size_t)(128 + kr) * D + 32 * dt + 8 * a + 4 * hl) = v4;
         }
       }
-    } else if (key < Lk) {
-      __bf16* dkrow = dk + koff + (size_t)key * rsk;
-      __bf16* dvrow = dv + koff + (size_t)key * rsk;
+    } else {
+      __bf16* out = role ? dk : dv;
+      const float sc = role ? scale : 1.f;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int h = 0; h < 2; ++h) {
+        const int kk = kb * 128 + 64 * kp + 32 * h + l32;
+        if (kk < Lk) {
+          __bf16* row = out + koff + (size_t)kk * rsk;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          *reinterpret_cast<bf16x4*>(dkrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dkacc[dt], a, scale);
-          *reinterpret_cast<bf16x4*>(dvrow + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(dvacc[dt], a, 1.f);
+          for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+              *reinterpret_cast<bf16x4*>(row + 32 * dt + 8 * a + 4 * hl) = acc_quad_bf16(acc[h][dt], a, sc);
+          }
         }
       }
     }
