@@ -19,10 +19,12 @@
 //   staged through LDS. S = Q K^T and dP = dO V^T put keys across lanes, so
 //   the accumulators become the B operands of dV^T += dO^T P and
 //   dK^T += Q^T dS directly; dO^T and Q^T are read transposed from LDS.
-// bf16 dQ kernel: workgroup = 4 waves x 32 query rows; the forward kernel's
-//   shape, with dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
-//   Launches of a few hundred query blocks use 8 waves per block instead,
-//   two groups that each walk half of its key tiles and add their dQ
+// bf16 dQ kernel: workgroup = 8 waves x 32 query rows, one per CU, sharing
+//   the staging of every K/V tile (block layouts, split and chunked walks:
+//   4 waves x 32 rows, two per CU); the forward kernel's orientation, with
+//   dP^T = V dO^T added and dQ^T += K^T dS^T in place of O^T.
+//   Launches of a few hundred query blocks use 8 waves per 128-row block
+//   instead, two groups that each walk half of its key tiles and add their dQ
 //   accumulators at the end (the longest block's walk sets their time), or
 //   cut every block's walk into chunks run by separate workgroups whose fp32
 //   partial sums a reduce kernel adds in chunk order, whichever a cost model
@@ -55,7 +57,7 @@ namespace ulysses {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr int kDqXcdRun = 64;   // one-walk dQ workgroups an XCD holds at once (two per CU)
+constexpr int kDqXcdRun = 32;   // one-walk dQ workgroups an XCD holds at once (one per CU)
 
 // Chunked causal walks (common.h): 128-row block x - 1 has 2x key tiles of
 // 64 under the causal mask, cut into ceil(x / t) parts of at most 2t tiles.
@@ -581,25 +583,28 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(
 // over the same 128 rows; group 0 walks the first half of the key tiles and
 // group 1 the second, each through its own K/V buffers, and group 0 adds
 // group 1's dQ accumulators to its own through LDS at the end.
-template <int D, bool CAUSAL, bool SPARSE, int NG = 1, bool CHUNK = false>
-__global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
+template <int D, bool CAUSAL, bool SPARSE, int NG = 1, bool CHUNK = false, int RW = 4>
+__global__ __launch_bounds__(64 * RW * NG, RW * NG == 4 ? 2 : 1) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ d_o, const float* __restrict__ lse, const float* __restrict__ delta,
     __bf16* __restrict__ dq, int Lq, int Lk, int Hq, int Hk, int G, int nqb, int nhb, float sl2, float scale,
     const uint8_t* __restrict__ layout, int nb, int ck, float* __restrict__ part) {
   static_assert(NG == 1 || (NG == 2 && !SPARSE), "split key walks are for dense attention");
   static_assert(!CHUNK || (NG == 1 && !SPARSE), "chunked key walks are for dense attention");
-  constexpr int BM = 128, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / 256, RSTEP = 256 / CPR;
+  static_assert((RW == 8) == (NG == 1 && !CHUNK && !SPARSE), "256-row blocks exactly for dense one-walk launches");
+  constexpr int TPG = 64 * RW;             // threads of one key-walk group, which stage its tiles
+  constexpr int BM = 32 * RW, BN = 64, KS = D / 16, DT = D / 32, CPR = D / 8, CH = BN * CPR / TPG,
+                RSTEP = TPG / CPR;
   constexpr int KST = Stride<D>::both;  // K: rows for S^T = K Q^T, transposed for dQ^T += K^T dS^T
   constexpr int VST = Stride<D>::row;   // V: rows for dP^T = V dO^T
   __shared__ __attribute__((aligned(16))) __bf16 Ks[2 * NG][BN * KST];
   __shared__ __attribute__((aligned(16))) __bf16 Vs[2 * NG][BN * VST];
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;   // row group of this wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (RW - 1);   // row group of this wave
   const int grp = NG == 2 ? __builtin_amdgcn_readfirstlane(tid >> 8) : 0;   // key half (NG = 2)
   // jobs (query block, head pair), longest rows first; the dense one-walk
-  // launch takes them in runs of 64 per XCD (two workgroups per CU), so that
+  // launch takes them in runs of 32 per XCD (one workgroup per CU), so that
   // the blocks on one XCD walk the same key tiles a few steps apart and
   // share them through its L2
   int rank = (int)blockIdx.x / nhb;
@@ -657,7 +662,7 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
 
   const int kend = CAUSAL ? min(Lk, q0 + BM) : Lk;
   const int nkb = (kend + BN - 1) / BN;
-  const int srow = (tid & 255) / CPR, scol = (tid % CPR) * 8;
+  const int srow = (tid & (TPG - 1)) / CPR, scol = (tid % CPR) * 8;
   const uint32_t head_bytes = (uint32_t)((size_t)Lk * rsk * 2);
   const __amdgpu_buffer_rsrc_t krs = head_rsrc(kh, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = head_rsrc(vh, head_bytes);
@@ -706,10 +711,11 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
           dp = mfma32(va[ks], df[ks], dp);
         }
         // LDS reads run LOOK fragments ahead of the MFMAs that use them (the
-        // registers of this kernel leave room for 4, not for all 16; a few
-        // values live across the two tile loops go to scratch once per
-        // workgroup, outside the loops)
-        constexpr int LOOK = 4;
+        // registers of this kernel leave room for 8 in 256-row workgroups,
+        // whose staging holds half as much per thread, and for 4 in 128-row
+        // ones, where a few values live across the two tile loops go to
+        // scratch once per workgroup, outside the loops)
+        constexpr int LOOK = RW == 8 ? 8 : 4;
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK, 0);
 #pragma unroll
         for (int i = 0; i < 2 * KS - LOOK; ++i) {
@@ -762,8 +768,8 @@ __global__ __launch_bounds__(256 * NG, 2 / NG) void bwd_dq_bf16_kernel(
     store_tile(0);
     __syncthreads();
     if (nkb > 1) load_tile(1);
-    // as in the forward pass: only the last two key tiles (causal) or a ragged last tile need a mask
-    const int nsteady = CAUSAL ? max(0, nkb - 2) : (Lk % BN ? nkb - 1 : nkb);
+    // as in the forward pass: only the last BM / BN key tiles (causal) or a ragged last tile need a mask
+    const int nsteady = CAUSAL ? max(0, nkb - BM / BN) : (Lk % BN ? nkb - 1 : nkb);
     int kb = 0;
     for (; kb < nsteady; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, steady);
     for (; kb < nkb; ++kb) tile(kb & 1, kb, kb + 1 < nkb, kb + 2 < nkb ? kb + 2 : -1, edge);
@@ -1306,11 +1312,13 @@ hipError_t bwd_bf16(const void* q, const void* k, const void* v, const void* o, 
     hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false, 2>), dim3((unsigned)nqb * nhb), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
                        (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, 0, nullptr);
-  else
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false>), dim3(xcd_run_grid((long long)nqb * nhb, kDqXcdRun)),
-                       dim3(256), 0, stream,
+  else {
+    const int nqb2 = (s.Lq + 255) / 256;
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, CAUSAL, false, 1, false, 8>),
+                       dim3(xcd_run_grid((long long)nqb2 * nhb, kDqXcdRun)), dim3(512), 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)d_o, lse, delta,
-                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb, nhb, sl2, scale, nullptr, 0, 0, nullptr);
+                       (__bf16*)dq, s.Lq, s.Lk, s.Hq, s.Hk, G, nqb2, nhb, sl2, scale, nullptr, 0, 0, nullptr);
+  }
   return hipGetLastError();
 }
 
