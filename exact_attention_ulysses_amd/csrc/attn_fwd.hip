@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_sparse_bf16_kernel(
 
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    for (int e = 0; e < 16; ++e) mx = fmaxf(fmaxf(mx, s0[e]), s1[e]);   // v_max3_f32
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mcand = mx * sl2;
     // The running maximum is raised only when some row's maximum grew by more
@@ -365,7 +365,9 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, BN == 64 ? fmaxf(s0[e], s1[e]) : s0[e]);
+    for (int e = 0; e < 16; e += 2)   // three-operand maxima (v_max3_f32)
+      mx = BN == 64 ? fmaxf(fmaxf(fmaxf(mx, s0[e]), s1[e]), fmaxf(s0[e + 1], s1[e + 1]))
+                    : fmaxf(fmaxf(mx, s0[e]), s0[e + 1]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mcand = mx * sl2;
     if (__ballot(mcand > m_run + 8.f)) {
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
+    for (int e = 0; e < 16; ++e) mx = fmaxf(fmaxf(mx, s0[e]), s1[e]);   // v_max3_f32
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mcand = mx * sl2;
     // lazy rescale, as in the four-wave kernel
