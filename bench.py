@@ -11,7 +11,8 @@ already resident in HBM:
                                                 gradient form, summing replicas)
 Prints ONE JSON line. `value` is attention fwd(+bwd) algorithmic TFLOP/s over
 the whole step time (transposes included); per-op figures come from HIP
-events recorded on the launch stream around every call in the timed steps.
+events recorded on the launch stream around every call in the timed steps,
+and `detail.sclk` is the graphics clock the host read (amdsmi) meanwhile.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -120,6 +121,57 @@ def load_traffic(workload: str, op: str):
         return None
     b = t["per_launch"][op]
     return b["read_bytes"] + b["write_bytes"]
+
+
+class ClockSampler:
+    """Samples the graphics clock of one GPU from the host (amdsmi) while the timed
+    steps run: the clock the chip holds under the load sets the MFMA rate, and it
+    differs from box to box. Failure to sample is reported, never fatal."""
+
+    def __init__(self, props, period_s: float = 0.02):
+        import threading
+        self.samples, self.error, self.period = [], None, period_s
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+        try:
+            import amdsmi
+            self._smi = amdsmi
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+            for h in amdsmi.amdsmi_get_processor_handles():
+                dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._h = h
+            if self._h is None:
+                self.error = f"no amdsmi device at PCI {want}"
+        except Exception as e:  # noqa: BLE001  (reported in the JSON line)
+            self.error = repr(e)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(float(self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.SYS)["clk"]))
+            except Exception as e:  # noqa: BLE001
+                self.error = repr(e)
+                return
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self._h is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self) -> dict:
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"error": self.error or "no samples"}
+        n = len(self.samples)
+        return {"mean_MHz": sum(self.samples) / n, "min_MHz": min(self.samples), "max_MHz": max(self.samples),
+                "samples": n, "source": "amdsmi graphics clock, sampled every 20 ms by the host during the timed steps"}
 
 
 def npairs(L: int, causal: bool, Lk: int = 0) -> int:
@@ -389,7 +441,9 @@ def main():
            for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    clocks = ClockSampler(torch.cuda.get_device_properties(dev))
     torch.cuda.synchronize()
+    clocks.start()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.steps):
@@ -397,6 +451,7 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    sclk = clocks.stop()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
     per_op = {}
@@ -435,6 +490,7 @@ def main():
         "transpose_GBps": perm_bytes / (perm_ms * 1e-3) / 1e9,
         "transpose_frac_peak": perm_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "wall_s_timed_region": wall,
+        "sclk": sclk,
     }
     if wl.backward:
         detail.update({"attn_bwd_ms": avg["attn_bwd"],

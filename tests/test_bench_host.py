@@ -1,6 +1,6 @@
 """Host-side logic of bench.py (no GPU needed): the flop counts behind the
-reported TFLOP/s, the guard that drops stale HBM traffic figures, and the
-refusal of multi-GPU runs."""
+reported TFLOP/s, the guard that drops stale HBM traffic figures, the
+refusal of multi-GPU runs and the clock sampler's fallback."""
 import importlib.util
 import json
 import os
@@ -85,3 +85,14 @@ def test_cpu_baseline_on_a_prefix(bench, backward):
         + 2 * len(names) * 2 * wl.tensor_bytes / (perm_bytes / r["perm_s"])
     assert r["extrapolated_full_s"] == pytest.approx(full)
     assert "extrapolated" in r["extrapolated_full_note"]
+
+
+def test_clock_sampler_reports_instead_of_failing(bench):
+    """Where amdsmi cannot reach the GPU (no device, or no device at that PCI
+    address) the clock sampler reports why in the JSON line; the bench goes on."""
+    import types
+    props = types.SimpleNamespace(pci_domain_id=0xFFFF, pci_bus_id=0xFF, pci_device_id=0x1F)
+    c = bench.ClockSampler(props)
+    c.start()
+    out = c.stop()
+    assert set(out) == {"error"} and out["error"]
