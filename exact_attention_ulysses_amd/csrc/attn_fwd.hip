@@ -50,7 +50,7 @@ namespace ulysses {
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kFwdXcdRun = 32;   // dense forward workgroups an XCD holds at once (one per CU)
+constexpr int kFwdXcdRun = 16;   // consecutive dense forward jobs per XCD (half of the 32 it holds at once)
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Block layouts: workgroup = 4 waves x 32 query rows, one 128-row query block;
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_split_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / WPG, wq = wave % WPG;
   const int gtid = tid % GT;                 // thread index within the group
-  // jobs (query block, head pair), longest rows first, in runs of 32 per
+  // jobs (query block, head pair), longest rows first, in runs of 16 per
   // XCD as in the ping-pong kernel
   int rank, hb;
   if (!xcd_run_block((int)blockIdx.x, kFwdXcdRun, nhb, nqb, &rank, &hb)) return;   // grid rounded up
@@ -494,9 +494,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool groupA = wave < 4;
   const int gtid = tid & 255;                // thread index within the group
-  // jobs (query block, head pair), longest rows first, in runs of 32 per XCD
-  // (one workgroup per CU): the blocks on one XCD walk the same key tiles a
-  // few steps apart and share them through its L2
+  // jobs (query block, head pair), longest rows first, in runs of 16 per XCD
+  // (an XCD holds 32 workgroups, one per CU, so two runs at once): the blocks
+  // of a run walk the same key tiles a few steps apart and share them
+  // through the XCD's L2; runs of 16 measured 0.3-0.9 % faster than 32
   int rank, hb;
   if (!xcd_run_block((int)blockIdx.x, kFwdXcdRun, nhb, nqb, &rank, &hb)) return;   // grid rounded up
   const int qb = nqb - 1 - rank;             // longest rows first
