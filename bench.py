@@ -134,10 +134,11 @@ class ClockSampler:
         self._stop = threading.Event()
         self._thread = None
         self._h = None
+        self._smi = None
         try:
             import amdsmi
-            self._smi = amdsmi
             amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            self._smi = amdsmi
             want = (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
             for h in amdsmi.amdsmi_get_processor_handles():
                 dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")
@@ -167,6 +168,12 @@ class ClockSampler:
         if self._thread is not None:
             self._stop.set()
             self._thread.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001  (the samples are already taken)
+                pass
+            self._smi = None
         if not self.samples:
             return {"error": self.error or "no samples"}
         n = len(self.samples)
