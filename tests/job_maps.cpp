@@ -74,7 +74,7 @@ static void check_xcd_runs() {
     if (taken != jobs) fail("xcd_run_block coverage", run, nhb, nranks, taken);
     ++launches;
   };
-  for (const int run : {32, 64}) {
+  for (const int run : {16, 32, 64}) {   // the runs the kernels take, and one more
     for (int nhb = 1; nhb <= 40; ++nhb)
       for (int nranks = 1; nranks <= 160; ++nranks) launch(run, nhb, nranks);
     for (const int nhb : {48, 64, 96, 128, 256, 512, 1024})

@@ -2,7 +2,7 @@
 
 tests/job_maps.cpp includes the library's own index helpers (the header the
 kernels use) and runs them over whole launches: the XCD-run job map covers
-every (block, head pair) job exactly once for 12,908 launch shapes, the
+every (block, head pair) job exactly once for 19,362 launch shapes, the
 chunked causal walks number every part of every block exactly once (longest
 blocks first) and the reduce kernels' slot formula finds each part where its
 work item wrote it, and the multiply-shift division agrees with `/` on 1.6 M
