@@ -178,7 +178,8 @@ class ClockSampler:
             return {"error": self.error or "no samples"}
         n = len(self.samples)
         return {"mean_MHz": sum(self.samples) / n, "min_MHz": min(self.samples), "max_MHz": max(self.samples),
-                "samples": n, "source": "amdsmi graphics clock, sampled every 20 ms by the host during the timed steps"}
+                "samples": n,
+                "source": f"amdsmi graphics clock, sampled every {self.period * 1e3:.0f} ms by the host during the timed steps"}
 
 
 def npairs(L: int, causal: bool, Lk: int = 0) -> int:
